@@ -1,0 +1,210 @@
+"""Pins of the DeepSelect method model (``oracle/model.py``).
+
+The model is checked against the oracle's plain definition, the pages' worked
+examples for its building blocks, the invariants and identities the
+DeepSelect deep-dive states, and the expected-work bound of its analysis.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import model
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    return json.load(open(os.path.join(GOLDEN, name)))
+
+
+# ---------------------------------------------------------------- building blocks
+
+def test_scan_worked_example():
+    g = _load("scan_example.json")
+    assert model.inclusive_scan(g["input"]).tolist() == g["inclusive"]
+    assert model.exclusive_scan(g["input"]).tolist() == g["exclusive"]
+
+
+def test_compact_worked_example():
+    g = _load("compact_example.json")
+    assert model.exclusive_scan(g["predicate"]).tolist() == g["exclusive_scan"]
+    out = model.compact(np.array(g["input"]), np.array(g["predicate"]))
+    assert out.tolist() == g["output"]
+
+
+def test_splitmix64_known_answer():
+    g = _load("splitmix64_seed0.json")
+    got = model.splitmix64(g["seed"], np.arange(3, dtype=np.uint64))
+    assert [int(v) for v in got] == [int(h, 16) for h in g["outputs_hex"]]
+
+
+def test_radix_select_against_sorting():
+    rng = np.random.default_rng(1)
+    for bits in (16, 32):
+        for n, k in ((1, 1), (10, 3), (1000, 1), (1000, 999), (5000, 700)):
+            hi = 1 << bits
+            ck = rng.integers(0, hi, n, dtype=np.uint64).astype(np.uint32)
+            if n > 10:
+                ck[: n // 3] = ck[0]  # force heavy ties
+            ci = np.arange(n)
+            kk, ki, kth = model.radix_select_topk(ck, ci, k, bits)
+            expect = np.sort(ck)[::-1][:k]
+            assert np.array_equal(np.sort(kk)[::-1], expect)
+            assert kth == int(expect[-1])
+            assert np.array_equal(ck[ki], kk)
+            # ties equal to the k-th are the earliest ones in buffer order
+            tie_pos = np.flatnonzero(ck == kth)
+            kept = np.sort(ki[kk == kth])
+            assert np.array_equal(kept, tie_pos[: len(kept)])
+
+
+# ---------------------------------------------------------------- block order
+
+def test_block_order_is_a_permutation():
+    for m in (1, 2, 7, 64, 149, 1024):
+        for seed in (0, 1, 123456789):
+            p = model.block_order(seed, 3, 0, np.arange(10, 10 + m))
+            assert sorted(p.tolist()) == list(range(10, 10 + m))
+
+
+def test_block_order_is_uniform():
+    """Chi-square test of the position of each block over many seeds."""
+    m = 8
+    counts = np.zeros((m, m))
+    trials = 20000
+    for seed in range(trials):
+        p = model.block_order(seed, 0, 0, np.arange(m))
+        counts[np.arange(m), p] += 1
+    expected = trials / m
+    chi2 = ((counts - expected) ** 2 / expected).sum()
+    # (m-1)^2 = 49 degrees of freedom; 99.9th percentile is about 85
+    assert chi2 < 85.0
+    # and all m! orders occur for a small m
+    seen = {tuple(model.block_order(s, 1, 0, np.arange(4)).tolist()) for s in range(2000)}
+    assert len(seen) == 24
+
+
+def test_block_order_depends_on_row_and_tag_not_on_data():
+    a = model.block_order(0, 0, 0, np.arange(64))
+    b = model.block_order(0, 1, 0, np.arange(64))
+    c = model.block_order(0, 0, 1, np.arange(64))
+    assert a.tolist() != b.tolist() and a.tolist() != c.tolist()
+
+
+# ---------------------------------------------------------------- model vs oracle
+
+SMALL = {"gauss4k": 1, "dsa32k": 4, "dsa128k_bf16": 3, "vocab152k_k64": 2,
+         "vocab152k_k1024": 2, "asc1m": 1, "ties1m": 1}
+
+
+def _check_row(x_row, res, o_vals, o_idx, k):
+    raw, _ = oracle.raw_bits(x_row)
+    assert len(res.idx) == k
+    assert len(set(res.idx.tolist())) == k
+    assert np.all((res.idx >= 0) & (res.idx < len(raw)))
+    assert np.array_equal(raw[res.idx], res.vals)
+    assert np.array_equal(np.sort(oracle.keys(res.vals)), np.sort(oracle.keys(o_vals)))
+    okeys = oracle.keys(raw)
+    kth = int(oracle.keys(o_vals).min())
+    if k == len(raw) or int((okeys > kth).sum()) + int((okeys == kth).sum()) == k:
+        assert sorted(res.idx.tolist()) == sorted(o_idx.tolist())
+    assert res.kth == kth
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_model_matches_oracle(name):
+    w = synth.WORKLOADS[name]
+    x = synth.generate(name, SMALL[name])
+    o_vals, o_idx = oracle.topk(x, w.k)
+    for r in range(x.shape[0]):
+        res = model.row_topk(x[r], w.k, w.block, w.block2, seed=0, row=r)
+        _check_row(x[r], res, o_vals[r], o_idx[r], w.k)
+        st = res.stats
+        # every element read exactly once, in blocks (deep-dive, Notes)
+        assert np.all(res.reads == 1)
+        # len(topk_candidate) <= k + B2 + B at all times; the check after every
+        # block makes the strict bound k + B2 + B - 1
+        assert st.max_len <= w.k + w.block + w.block2 - 1
+        # T only rises, and everything is admitted before the first compaction
+        assert all(a <= b for a, b in zip(st.thresholds, st.thresholds[1:]))
+        assert st.all_admitted_before_first_compaction
+        # W = A + kR and R*B2 <= A (analysis section)
+        assert st.W == st.A + w.k * st.R
+        assert st.R * w.block2 <= st.A
+
+
+@pytest.mark.parametrize("split", [2, 3, 8])
+def test_split_rows_match_oracle(split):
+    for name in ("dsa32k", "asc1m_b1", "dsa128k_bf16"):
+        w = synth.WORKLOADS[name]
+        x = synth.generate(name, 1)
+        o_vals, o_idx = oracle.topk(x, w.k)
+        res = model.row_topk(x[0], w.k, w.block, w.block2, seed=4, row=0, split=split)
+        _check_row(x[0], res, o_vals[0], o_idx[0], w.k)
+        assert np.all(res.reads == 1)
+        assert res.stats.W == res.stats.A + w.k * res.stats.R
+
+
+def test_edge_shapes_match_oracle():
+    cases = [
+        (1, 1, 1, 1), (5, 5, 2, 1), (37, 3, 4, 5), (100, 100, 7, 3), (1000, 1, 1, 1),
+        (1000, 17, 1000, 1000), (1001, 64, 256, 3), (4096, 64, 5000, 1),
+    ]
+    for n, k, b, b2 in cases:
+        for kind in ("gauss", "small_ints", "special"):
+            for dt in ("f32", "bf16"):
+                x = synth.random_rows(1, n, dt, n + k, kind)
+                o_vals, o_idx = oracle.topk(x, k)
+                res = model.row_topk(x[0], k, b, b2, seed=1)
+                _check_row(x[0], res, o_vals[0], o_idx[0], k)
+                assert res.stats.max_len <= k + b + b2 - 1
+
+
+def test_all_minus_inf_row_fills_the_buffer():
+    x = np.full((1, 3000), 0xFF80, dtype=np.uint16)
+    x[0, 17] = 0x3F80  # one finite value
+    o_vals, o_idx = oracle.topk(x, 100)
+    res = model.row_topk(x[0], 100, 256, 256)
+    _check_row(x[0], res, o_vals[0], o_idx[0], 100)
+    assert 17 in res.idx.tolist()
+
+
+# ---------------------------------------------------------------- analysis
+
+@pytest.mark.parametrize("name", ["gauss4k", "dsa32k", "dsa128k_bf16", "vocab152k_k64",
+                                  "vocab152k_k1024", "asc1m", "ties1m"])
+def test_mean_w_below_bound(name):
+    """E[W] <= (1 + k/B2)(k+B+B2)H_m over the random block order."""
+    w = synth.WORKLOADS[name]
+    rows = {"gauss4k": 1, "asc1m": 1, "ties1m": 1}.get(name, 2)
+    x = synth.generate(name, rows)
+    seeds = range(8) if w.n <= 200000 else range(3)
+    ws = [model.row_topk(x[r], w.k, w.block, w.block2, seed=s, row=r).stats.W
+          for r in range(rows) for s in seeds]
+    bound = model.expected_w_bound(w.n, w.k, w.block, w.block2)
+    assert np.mean(ws) <= bound
+    assert max(ws) <= 1.5 * bound
+
+
+def test_block_order_changes_cost_not_result():
+    w = synth.WORKLOADS["dsa32k"]
+    x = synth.generate("dsa32k", 1)[0]
+    ref = None
+    for seed in range(10):
+        res = model.row_topk(x, w.k, w.block, w.block2, seed=seed)
+        got = sorted(res.vals.view(np.float32).tolist())
+        ref = ref or got
+        assert got == ref
+    # in-order scan (the identity order) of an ascending row: same answer,
+    # far more work than the random order
+    asc = synth.generate("asc1m", 1)[0][: 1 << 17]
+    keys = oracle.keys(asc)
+    blocks = [(keys[lo:lo + 1024], np.arange(lo, lo + 1024)) for lo in range(0, len(asc), 1024)]
+    ck, ci, kth, st = model.deepselect(blocks, 512, 1024, 32)
+    assert sorted(ci.tolist()) == list(range(len(asc) - 512, len(asc)))
+    rnd = model.row_topk(asc, 512, 1024, 1024, seed=0)
+    assert st.W > 10 * rnd.stats.W
