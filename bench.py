@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of DeepSelect batched row-wise top-k on one MI355X.
+
+One step = one deepselect_topk call over a whole batch (every block of every row
+streamed once, filtered, compacted, and the k results written). The default
+workload is the long-context DSA indexer case: 128 rows x 131072 bfloat16 scores
+(causal -inf tails), k = 2048, B = B2 = 2048.
+
+Timing
+  * inputs are resident in HBM: R rotating copies of the batch (R*size >= the
+    --rotate-mb budget, default 768 MiB, three times the 256 MiB Infinity Cache)
+    so every launch reads rows that are not cached;
+  * W untimed warm-up steps, then exactly K steps bracketed by a device
+    synchronisation on both sides; each launch is also bracketed by its own pair
+    of HIP events on the launch stream, which gives the kernel's average
+    duration for the roofline;
+  * value = batch*N / (region time / K) in Gelem/s (whole job, one GPU).
+
+Extras in the JSON line: the roofline of the kernel (HBM-bound; algorithmic
+bytes = input read once + k (value, index) pairs per row), the CPU oracle timed
+on this host, and torch.topk on the same buffers.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "top-k Gelem/s and HBM GB/s (% of peak), batch×N rows, k=512/2048"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "top_selection_row_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"deepselect_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_digest") != source_digest():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(workload: str, seconds: float):
+    import numpy as np
+
+    import oracle
+    import synth
+
+    w = synth.WORKLOADS[workload]
+    threads = max(1, min(16, os.cpu_count() or 1))
+    rows = min(w.batch, 64)
+    x = synth.generate(workload, rows)
+    oracle.topk(x[:1], w.k, nthreads=1)  # load + warm
+    done, t0 = 0, time.perf_counter()
+    while True:
+        oracle.topk(x, w.k, nthreads=threads)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    gelem = done * rows * w.n / el / 1e9
+    del np
+    return {"value": round(gelem, 4), "unit": "Gelem/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} passes of the oracle (C full sort) over {rows} of the {w.batch} "
+                      f"rows, {el:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="dsa128k_bf16")
+    ap.add_argument("--split", type=int, default=0, help="parts per row (0 = library choice)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--rotate-mb", type=int, default=768)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-torch", action="store_true", help="skip the torch.topk comparison")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the DeepSelect path here has no multi-GPU leg "
+              "(rows shard across GPUs without communication). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    import top_selection_row_amd as ds
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    dt = ds.DS_F32 if w.dtype == "f32" else ds.DS_BF16
+    es = w.elem_bytes
+
+    log(f"[bench] generating {args.workload}: {w.batch} x {w.n} {w.dtype}")
+    x = synth.generate(args.workload)
+    size = x.nbytes
+    copies = max(2, math.ceil(args.rotate_mb * 2**20 / size))
+    if w.dtype == "f32":
+        xt = torch.from_numpy(x).to(dev)
+    else:
+        xt = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    rot = torch.empty((copies, w.batch, w.n), dtype=xt.dtype, device=dev)
+    for i in range(copies):
+        rot[i].copy_(xt)
+    del xt
+    vals = torch.empty((w.batch, w.k), dtype=rot.dtype, device=dev)
+    idx = torch.empty((w.batch, w.k), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    split = args.split or ds.deepselect_plan_split(dt, w.batch, w.n, w.k, w.block, w.block2,
+                                                   props.multi_processor_count)
+    if split < 1:
+        log(f"[bench] no valid split: {ds.deepselect_status_string(split)}")
+        return 1
+    lib = ds.library()
+    opt = ds.DsOptions(int(split), 0, None, None, 0)
+    ptrs = [rot[i].data_ptr() for i in range(copies)]
+    vptr, iptr = vals.data_ptr(), idx.data_ptr()
+    fn = lib.deepselect_topk_ex
+    seed = args.seed
+
+    def step(i):
+        rc = fn(ptrs[i % copies], dt, w.batch, w.n, w.n, w.k, w.block, w.block2, seed, vptr, iptr, sptr,
+                ctypes.byref(opt))
+        if rc != 0:
+            raise RuntimeError(f"deepselect_topk_ex failed: {ds.deepselect_status_string(rc)}")
+
+    log(f"[bench] {copies} rotating copies ({copies * size / 2**20:.0f} MiB), split {split}, "
+        f"{args.warmup} warm-up + {args.steps} timed steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    r0.record(stream)
+    for i in range(K):
+        ev0[i].record(stream)
+        step(args.warmup + i)
+        ev1[i].record(stream)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    region_ms = r0.elapsed_time(r1)
+    kern_ms = sorted(a.elapsed_time(b) for a, b in zip(ev0, ev1))
+    kern_avg_ms = sum(kern_ms) / K
+    kern_med_ms = kern_ms[K // 2]
+    ms_per_step = region_ms / K
+    elems = w.batch * w.n
+    value = elems / (ms_per_step * 1e-3) / 1e9
+    alg_bytes = w.batch * w.n * es + w.batch * w.k * (es + 4)
+    achieved = alg_bytes / (kern_avg_ms * 1e-3) / 1e9
+    log(f"[bench] region {region_ms:.3f} ms for {K} steps (wall {wall * 1e3:.1f} ms); kernel avg "
+        f"{kern_avg_ms * 1e3:.2f} us, median {kern_med_ms * 1e3:.2f} us; {achieved:.0f} GB/s")
+
+    torch_info = None
+    if not args.no_torch:
+        tk = {}
+        for srt in (False, True):
+            for i in range(3):
+                torch.topk(rot[i % copies], w.k, dim=-1, largest=True, sorted=srt)
+            torch.cuda.synchronize()
+            reps = min(50, K)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(reps):
+                torch.topk(rot[i % copies], w.k, dim=-1, largest=True, sorted=srt)
+            b.record(stream)
+            torch.cuda.synchronize()
+            tk["sorted_us" if srt else "unsorted_us"] = round(a.elapsed_time(b) / reps * 1e3, 2)
+        torch_info = tk
+        log(f"[bench] torch.topk: {tk}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload, args.cpu_seconds)
+        log(f"[bench] cpu oracle: {cpu}")
+
+    traffic = measured_traffic(args.workload)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16" if w.dtype == "bf16" else "u32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": w.batch, "N": w.n, "input_dtype": w.dtype,
+                   "k": w.k, "B": w.block, "B2": w.block2, "split": int(split),
+                   "rotating_copies": copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "kernel_us": {"avg": round(kern_avg_ms * 1e3, 3), "median": round(kern_med_ms * 1e3, 3)},
+        "cpu_baseline": cpu,
+        "torch_topk": torch_info,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,130 @@
+/*
+ * deepselect.h -- C ABI of the MI355X (gfx950) DeepSelect batched row-wise top-k.
+ *
+ * The operation is DeepSelectTopk of the DeepSelect deep-dive (PFCCLab/DeepSelect,
+ * section "算法"): for each row, scan its B-element blocks once in a random order
+ * that does not depend on the data, admit the elements greater than a rising
+ * threshold T into an on-chip candidate buffer, and whenever the buffer holds
+ * k + B2 or more entries shrink it to its k largest with a radix select and set
+ * T to the k-th value. The last step selects k once more. The result is exactly
+ * the k largest values of the row (the "Top K Selection" problem of
+ * "CUDA 算子笔记 4", milkfeng.top).
+ *
+ * Conventions shared by every entry point
+ *   - All pointers named x, out_vals, out_idx, stats and workspace are DEVICE
+ *     pointers on the current HIP device. The library never copies them to the
+ *     host and never frees them; the caller owns them.
+ *   - Row r of the input is x[r*row_stride .. r*row_stride + N) (row_stride in
+ *     elements, >= N). Elements are float32 (DS_F32) or bfloat16 (DS_BF16).
+ *   - Output row r is out_vals[r*k .. r*k+k) (same element type as x, the exact
+ *     bit pattern of the chosen input element) and out_idx[r*k .. r*k+k) (int32
+ *     column in [0, N)). The k entries of a row come in no particular order.
+ *     When several elements tie at the k-th value any of them may be returned;
+ *     the choice is deterministic for a given input, k, B, B2, seed and split.
+ *   - Values are ordered by the order-preserving unsigned key of "CUDA 算子笔记 4"
+ *     section "改造 Radix Sort" (float_to_key): float order, with -0 < +0, a
+ *     positive NaN above +inf and a negative NaN below -inf.
+ *   - seed fixes the random block order (a SplitMix64 hash of seed, row and
+ *     block id, sorted); the result set does not depend on it, the cost does.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream). Results are valid after the stream reaches the call; x must not
+ *     change before then. Nothing is copied device-to-host.
+ *   - Every argument is checked on the host before any HIP call; a rejected call
+ *     enqueues nothing. No C++ exception crosses this interface.
+ *   - Entry points are thread-safe. Calls that share a library-owned workspace
+ *     (same device and stream) are ordered by their stream.
+ */
+#ifndef DEEPSELECT_H
+#define DEEPSELECT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DS_F32 = 0, DS_BF16 = 1 } ds_dtype_t;
+
+typedef enum {
+    DS_OK = 0,
+    DS_ERR_NULL = -1,        /* a required pointer is NULL */
+    DS_ERR_DTYPE = -2,       /* dtype not DS_F32 / DS_BF16 */
+    DS_ERR_SHAPE = -3,       /* batch < 0, N < 1, N >= 2^31, row_stride < N, misaligned x */
+    DS_ERR_K = -4,           /* k < 1 or k > N (the pseudo-code's require line) */
+    DS_ERR_BLOCK = -5,       /* B < 1 or B2 < 1, or a forced split the row cannot take */
+    DS_ERR_UNSUPPORTED = -6, /* on-chip buffer k+B+B2 (or the block order) exceeds LDS */
+    DS_ERR_HIP = -7,         /* a HIP call failed (allocation, attribute, launch) */
+    DS_ERR_WORKSPACE = -8    /* caller workspace smaller than deepselect_workspace_bytes */
+} ds_status_t;
+
+/* Per-row statistics written when ds_options_t.stats is set: four uint64 per row,
+ * in this order (the quantities of the deep-dive's section
+ * "RadixSelectTopK 总处理元素数的期望上界"):
+ *   W        total input length of every RadixSelectTopK call, the final one included
+ *   A        elements admitted into the candidate buffer
+ *   R        RadixSelectTopK calls inside the loop (compactions)
+ *   MAX_LEN  largest candidate-buffer length reached
+ * With split > 1 the row's figures add up its parts and the merge (MAX_LEN: max). */
+enum { DS_STAT_W = 0, DS_STAT_A = 1, DS_STAT_R = 2, DS_STAT_MAX_LEN = 3, DS_STATS_PER_ROW = 4 };
+
+typedef struct ds_options {
+    /* Parts per row (the deep-dive's "实现" section, last paragraph: a row cut into
+     * parts whose top-k are gathered and reduced). 0 = library choice
+     * (deepselect_plan_split with the device's compute-unit count). A forced value
+     * must satisfy 1 <= split <= ceil(N/B) and leave every part >= k elements,
+     * else DS_ERR_BLOCK. */
+    int32_t split;
+    int32_t reserved0;
+    /* Device pointer to batch*4 uint64 (layout above), or NULL for no statistics. */
+    uint64_t *stats;
+    /* Device workspace for split rows, or NULL for the library-owned one.
+     * Size from deepselect_workspace_bytes. A caller workspace must be
+     * zero-filled before its first use; every call leaves it zero-filled where
+     * that matters (its arrival counters reset themselves). */
+    void *workspace;
+    size_t workspace_bytes;
+} ds_options_t;
+
+/* Check arguments only (pure host code, no HIP call; usable without a GPU).
+ * Returns DS_OK or the status deepselect_topk would return before launching. */
+int deepselect_validate(int dtype, int64_t batch, int64_t N, int64_t row_stride, int32_t k,
+                        int32_t B, int32_t B2);
+
+/* Batched row-wise top-k of x[batch][N] (see the conventions above). */
+int deepselect_topk(const void *x, int dtype, int64_t batch, int64_t N, int64_t row_stride,
+                    int32_t k, int32_t B, int32_t B2, uint64_t seed, void *out_vals,
+                    int32_t *out_idx, void *stream);
+
+/* deepselect_topk with options (forced split, statistics, caller workspace).
+ * opt may be NULL (then identical to deepselect_topk). */
+int deepselect_topk_ex(const void *x, int dtype, int64_t batch, int64_t N, int64_t row_stride,
+                       int32_t k, int32_t B, int32_t B2, uint64_t seed, void *out_vals,
+                       int32_t *out_idx, void *stream, const ds_options_t *opt);
+
+/* The split factor the library picks for this shape on a device with num_cus
+ * compute units (pure host code). Returns >= 1, or a negative status. */
+int deepselect_plan_split(int dtype, int64_t batch, int64_t N, int32_t k, int32_t B, int32_t B2,
+                          int32_t num_cus);
+
+/* Workspace bytes a call with this shape and split needs (0 when split == 1).
+ * Pure host code. Returns 0 for invalid arguments as well. */
+size_t deepselect_workspace_bytes(int dtype, int64_t batch, int64_t N, int32_t k, int32_t B,
+                                  int32_t B2, int32_t split);
+
+/* Dynamic LDS bytes one workgroup of this shape uses (pure host code; 0 if invalid). */
+size_t deepselect_lds_bytes(int dtype, int64_t N, int32_t k, int32_t B, int32_t B2,
+                            int32_t split);
+
+/* Static description of a status code (never NULL). */
+const char *deepselect_status_string(int status);
+
+/* Free every library-owned workspace (all devices and streams). Must not be
+ * called while a call using one is still queued. */
+void deepselect_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DEEPSELECT_H */

@@ -1,0 +1,103 @@
+"""The C-ABI library: it loads without a GPU, exports every declared entry point,
+and its pure-host functions (validation, split plan, sizes) behave as the header
+says. No compute call is made here."""
+import math
+import os
+import re
+
+import pytest
+
+import synth
+import top_selection_row_amd as ds
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "deepselect.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(deepselect_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ds.library()
+    names = declared_functions()
+    assert set(names) == set(ds.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("args,status", [
+    ((ds.DS_F32, 4, 100, 100, 10, 32, 32), ds.DS_OK),
+    ((7, 4, 100, 100, 10, 32, 32), ds.DS_ERR_DTYPE),
+    ((ds.DS_F32, -1, 100, 100, 10, 32, 32), ds.DS_ERR_SHAPE),
+    ((ds.DS_F32, 4, 0, 100, 10, 32, 32), ds.DS_ERR_SHAPE),
+    ((ds.DS_F32, 4, 100, 99, 10, 32, 32), ds.DS_ERR_SHAPE),
+    ((ds.DS_F32, 4, 1 << 31, 1 << 31, 10, 32, 32), ds.DS_ERR_SHAPE),
+    ((ds.DS_F32, 4, 100, 100, 0, 32, 32), ds.DS_ERR_K),
+    ((ds.DS_F32, 4, 100, 100, 101, 32, 32), ds.DS_ERR_K),
+    ((ds.DS_F32, 4, 100, 100, 10, 0, 32), ds.DS_ERR_BLOCK),
+    ((ds.DS_F32, 4, 100, 100, 10, 32, 0), ds.DS_ERR_BLOCK),
+    ((ds.DS_BF16, 4, 1 << 20, 1 << 20, 10000, 10000, 10000), ds.DS_ERR_UNSUPPORTED),
+    ((ds.DS_BF16, 0, 100, 100, 10, 32, 32), ds.DS_OK),
+])
+def test_validate(args, status):
+    assert ds.deepselect_validate(*args) == status
+
+
+def test_topk_rejects_before_any_hip_call():
+    # argument errors come back without touching a device (none exists here)
+    assert ds.deepselect_topk(0, ds.DS_F32, 2, 64, 64, 8, 16, 16, 0, 0, 0, 0) == ds.DS_ERR_NULL
+    assert ds.deepselect_topk(16, ds.DS_F32, 2, 64, 64, 65, 16, 16, 0, 16, 16, 0) == ds.DS_ERR_K
+    assert ds.deepselect_topk(16, 5, 2, 64, 64, 8, 16, 16, 0, 16, 16, 0) == ds.DS_ERR_DTYPE
+    assert ds.deepselect_topk(0, ds.DS_F32, 0, 64, 64, 8, 16, 16, 0, 0, 0, 0) == ds.DS_OK
+    # element-misaligned x
+    assert ds.deepselect_topk(18, ds.DS_F32, 2, 64, 64, 8, 16, 16, 0, 16, 16, 0) == ds.DS_ERR_SHAPE
+
+
+def test_status_strings():
+    for st in range(0, -9, -1):
+        s = ds.deepselect_status_string(st)
+        assert s and s != "unknown status"
+    assert ds.deepselect_status_string(-99) == "unknown status"
+
+
+def _parts_ok(n, k, B, S):
+    m = -(-n // B)
+    for s in range(S):
+        b0, b1 = s * m // S, (s + 1) * m // S
+        if min(b1 * B, n) - b0 * B < k:
+            return False
+    return True
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_split_plan_is_valid(name):
+    w = synth.WORKLOADS[name]
+    dt = ds.DS_F32 if w.dtype == "f32" else ds.DS_BF16
+    S = ds.deepselect_plan_split(dt, w.batch, w.n, w.k, w.block, w.block2, 256)
+    assert S >= 1
+    if S > 1:
+        assert _parts_ok(w.n, w.k, w.block, S)
+        assert ds.deepselect_workspace_bytes(dt, w.batch, w.n, w.k, w.block, w.block2, S) >= \
+            w.batch * S * w.k * 8 + w.batch * 4
+    lds = ds.deepselect_lds_bytes(dt, w.n, w.k, w.block, w.block2, S)
+    L = w.k + w.block + w.block2 - 1
+    assert L * (w.elem_bytes + 4) <= lds <= 160 * 1024
+    # enough workgroups for 256 compute units unless the batch already has them
+    if w.batch < 256:
+        assert w.batch * S >= min(256, w.batch * math.floor(math.sqrt(w.n * w.elem_bytes / (8 * w.k))))
+
+
+def test_split_plan_examples():
+    assert ds.deepselect_plan_split(ds.DS_BF16, 128, 131072, 2048, 2048, 2048, 256) == 2
+    assert ds.deepselect_plan_split(ds.DS_F32, 64, 32768, 512, 1024, 1024, 256) == 4
+    assert ds.deepselect_plan_split(ds.DS_F32, 256, 151936, 64, 1024, 1024, 256) == 1
+    assert ds.deepselect_plan_split(ds.DS_F32, 32, 1 << 20, 512, 1024, 1024, 256) == 8
+    assert ds.deepselect_plan_split(ds.DS_F32, 1, 1 << 20, 512, 1024, 1024, 256) == 32
+
+
+def test_workspace_zero_without_split():
+    assert ds.deepselect_workspace_bytes(ds.DS_F32, 8, 1000, 10, 100, 100, 1) == 0
+    assert ds.deepselect_workspace_bytes(ds.DS_F32, 8, 1000, 0, 100, 100, 2) == 0

@@ -1,0 +1,235 @@
+"""GPU parity: the HIP DeepSelect path against the CPU oracle, through the C ABI.
+
+Acceptance per row (bit-exact; no floating-point arithmetic happens on either
+side, every comparison is an integer comparison of order-preserving keys):
+  1. exactly k entries, indices distinct and in [0, N);
+  2. each returned value is bit-identical to x[row, idx];
+  3. the multiset of returned keys equals the oracle's;
+  4. when the k-th value does not tie across the cut, the index set equals the
+     oracle's (with a tie, several index sets are correct and (1)-(3) decide).
+W, A, R and max_len per row must equal the method model's exactly: they do not
+depend on which tied elements survive, only on the block order and the data.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import model
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("no GPU", allow_module_level=True)
+
+import top_selection_row_amd as ds  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(x: np.ndarray):
+    if x.dtype == np.float32:
+        return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def raw_of(t):
+    if t.dtype == torch.float32:
+        return t.cpu().numpy().view(np.uint32)
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    raise TypeError(t.dtype)
+
+
+def run_gpu(x: np.ndarray, k, B, B2, seed=0, split=0, stats=True):
+    xt = to_device(x)
+    out = ds.topk(xt, k, B, B2, seed, split=split, stats=stats)
+    torch.cuda.synchronize()
+    vals, idx = raw_of(out[0]), out[1].cpu().numpy()
+    st = out[2].cpu().numpy() if stats else None
+    return vals, idx, st
+
+
+def check_rows(x: np.ndarray, vals, idx, k, rows=None):
+    raw, _ = oracle.raw_bits(x)
+    o_vals, o_idx = oracle.topk(x, k)
+    rows = range(x.shape[0]) if rows is None else rows
+    n = x.shape[1]
+    for r in rows:
+        assert idx[r].shape == (k,)
+        assert len(np.unique(idx[r])) == k, f"row {r}: repeated index"
+        assert idx[r].min() >= 0 and idx[r].max() < n, f"row {r}: index out of range"
+        assert np.array_equal(raw[r][idx[r]], vals[r]), f"row {r}: value bits differ from x[idx]"
+        got = np.sort(oracle.keys(vals[r]))
+        want = np.sort(oracle.keys(o_vals[r]))
+        assert np.array_equal(got, want), f"row {r}: top-k multiset differs from the oracle"
+        keys_r = oracle.keys(raw[r])
+        kth = want[0]
+        if k == n or int((keys_r >= kth).sum()) == k:
+            assert np.array_equal(np.sort(idx[r]), np.sort(o_idx[r])), f"row {r}: index set differs"
+
+
+def check_stats_against_model(x, st, k, B, B2, seed, split, rows):
+    for r in rows:
+        res = model.row_topk(x[r], k, B, B2, seed=seed, row=r, split=split)
+        want = (res.stats.W, res.stats.A, res.stats.R, res.stats.max_len)
+        assert tuple(int(v) for v in st[r]) == want, f"row {r}: (W, A, R, max_len) {tuple(st[r])} != model {want}"
+
+
+def plan(w):
+    dt = ds.DS_F32 if w.dtype == "f32" else ds.DS_BF16
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return ds.deepselect_plan_split(dt, w.batch, w.n, w.k, w.block, w.block2, cus)
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workload_full_size(name):
+    w = synth.WORKLOADS[name]
+    log(f"[gpu] workload {name}: batch {w.batch} N {w.n} {w.dtype} k {w.k} B {w.block} B2 {w.block2}")
+    x = synth.generate(name)
+    S = plan(w)
+    vals, idx, st = run_gpu(x, w.k, w.block, w.block2, seed=0, split=0)
+    check_rows(x, vals, idx, w.k)
+    rows = range(min(w.batch, 6))
+    check_stats_against_model(x, st, w.k, w.block, w.block2, 0, S, rows)
+    assert np.all(st[:, 3] <= max(w.k + w.block + w.block2 - 1, 2 * w.k + w.block2 - 1))
+
+
+@pytest.mark.parametrize("name,split", [("dsa32k", 1), ("dsa32k", 2), ("dsa32k", 8),
+                                        ("dsa128k_bf16", 1), ("dsa128k_bf16", 4),
+                                        ("asc1m_b1", 8), ("asc1m_b1", 64), ("gauss4k", 3),
+                                        ("vocab152k_k1024", 2)])
+def test_forced_split(name, split):
+    w = synth.WORKLOADS[name]
+    rows = min(w.batch, 16)
+    log(f"[gpu] forced split {name} S={split} rows {rows}")
+    x = synth.generate(name, rows)
+    vals, idx, st = run_gpu(x, w.k, w.block, w.block2, seed=3, split=split)
+    check_rows(x, vals, idx, w.k)
+    check_stats_against_model(x, st, w.k, w.block, w.block2, 3, split, range(min(rows, 4)))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 2**63 + 5])
+def test_seeds_and_determinism(seed):
+    w = synth.WORKLOADS["dsa128k_bf16"]
+    log(f"[gpu] seed {seed} on dsa128k_bf16 (16 rows)")
+    x = synth.generate("dsa128k_bf16", 16)
+    a = run_gpu(x, w.k, w.block, w.block2, seed=seed)
+    b = run_gpu(x, w.k, w.block, w.block2, seed=seed)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+    check_rows(x, a[0], a[1], w.k)
+    check_stats_against_model(x, a[2], w.k, w.block, w.block2, seed, plan(synth.Workload(
+        "t", 16, w.n, w.dtype, w.k, w.block, w.block2, 0, "", "")), range(3))
+
+
+# ---------------------------------------------------------------- edge cases
+
+EDGE = [
+    # (batch, N, k, B, B2, dtype, kind)
+    (3, 1, 1, 1, 1, "f32", "gauss"),
+    (2, 5, 5, 2, 1, "f32", "gauss"),        # k = N
+    (4, 37, 1, 4, 5, "bf16", "small_ints"),  # k = 1, tiny blocks
+    (3, 1000, 17, 1000, 1000, "f32", "special"),  # one block (N <= B)
+    (2, 1001, 64, 256, 3, "f32", "gauss"),   # ragged last block, B2 != B
+    (2, 4096, 64, 5000, 1, "bf16", "gauss"),  # N < B, B2 = 1
+    (5, 3000, 100, 96, 40, "bf16", "special"),
+    (2, 65536 + 3, 300, 1000, 700, "f32", "small_ints"),  # odd N: scalar loads
+    (2, 12345, 2048, 2048, 2048, "bf16", "gauss"),
+    (1, 200000, 1, 3072, 1, "f32", "gauss"),  # several tiles per block
+    (2, 9000, 600, 7, 9, "f32", "gauss"),     # more than 1024 blocks -> split lower bound
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"{c[0]}x{c[1]}k{c[2]}B{c[3]}B2{c[4]}{c[5]}{c[6]}" for c in EDGE])
+def test_edge_shapes(case):
+    batch, n, k, B, B2, dt, kind = case
+    log(f"[gpu] edge {case}")
+    x = synth.random_rows(batch, n, dt, 77, kind)
+    if ds.deepselect_validate(ds.DS_F32 if dt == "f32" else ds.DS_BF16, batch, n, n, k, B, B2) != 0:
+        pytest.skip("shape outside the library's LDS limits")
+    vals, idx, st = run_gpu(x, k, B, B2, seed=9)
+    check_rows(x, vals, idx, k)
+
+
+def test_all_minus_inf_and_nan_rows():
+    n, k = 5000, 300
+    x = np.full((4, n), 0xFF80, dtype=np.uint16)  # all -inf
+    x[1, 4321] = 0x3F80
+    x[2, ::7] = 0x7FC0  # +NaN above +inf
+    x[3, ::5] = 0xFFC0  # -NaN below -inf
+    x[3, 3::11] = 0x8000  # -0
+    x[3, 4::13] = 0x0000  # +0
+    log("[gpu] -inf / NaN / signed-zero rows")
+    vals, idx, st = run_gpu(x, k, 512, 512)
+    check_rows(x, vals, idx, k)
+
+
+def test_row_stride_and_misaligned_base():
+    w = synth.WORKLOADS["dsa32k"]
+    x = synth.generate("dsa32k", 8)
+    o_vals, o_idx = oracle.topk(x, w.k)
+    big = np.zeros((8, w.n + 40), dtype=np.float32)
+    big[:, 1:w.n + 1] = x  # row_stride N+40, base offset by one element
+    t = torch.from_numpy(big).to(DEV)
+    view = t[:, 1:w.n + 1]
+    log("[gpu] strided, element-misaligned view")
+    vals = torch.empty((8, w.k), dtype=torch.float32, device=DEV)
+    idx = torch.empty((8, w.k), dtype=torch.int32, device=DEV)
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = ds.deepselect_topk(view.data_ptr(), ds.DS_F32, 8, w.n, w.n + 40, w.k, w.block, w.block2, 0,
+                            vals.data_ptr(), idx.data_ptr(), stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    check_rows(x, vals.cpu().numpy().view(np.uint32), idx.cpu().numpy(), w.k)
+
+
+def test_non_default_stream_and_batch_zero():
+    w = synth.WORKLOADS["gauss4k"]
+    x = synth.generate("gauss4k")
+    s = torch.cuda.Stream()
+    log("[gpu] side stream")
+    with torch.cuda.stream(s):
+        xt = to_device(x)
+        vals, idx = ds.topk(xt, w.k, w.block, w.block2)
+    s.synchronize()
+    check_rows(x, raw_of(vals), idx.cpu().numpy(), w.k)
+    empty = torch.empty((0, 100), dtype=torch.float32, device=DEV)
+    v, i = ds.topk(empty, 5, 10, 10)
+    assert v.shape == (0, 5)
+
+
+def test_caller_workspace():
+    w = synth.WORKLOADS["dsa32k"]
+    x = synth.generate("dsa32k", 16)
+    xt = to_device(x)
+    S = 4
+    nbytes = ds.deepselect_workspace_bytes(ds.DS_F32, 16, w.n, w.k, w.block, w.block2, S)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    vals = torch.empty((16, w.k), dtype=torch.float32, device=DEV)
+    idx = torch.empty((16, w.k), dtype=torch.int32, device=DEV)
+    stream = torch.cuda.current_stream().cuda_stream
+    log("[gpu] caller workspace, two calls")
+    for _ in range(2):
+        rc = ds.deepselect_topk_ex(xt.data_ptr(), ds.DS_F32, 16, w.n, w.n, w.k, w.block, w.block2, 0,
+                                   vals.data_ptr(), idx.data_ptr(), stream, split=S,
+                                   workspace=ws.data_ptr(), workspace_bytes=nbytes)
+        assert rc == 0
+        torch.cuda.synchronize()
+        check_rows(x, vals.cpu().numpy().view(np.uint32), idx.cpu().numpy(), w.k)
+    # arrival counters are back to zero after the call
+    assert int(ws[: 16 * 4].sum().item()) == 0
+    rc = ds.deepselect_topk_ex(xt.data_ptr(), ds.DS_F32, 16, w.n, w.n, w.k, w.block, w.block2, 0,
+                               vals.data_ptr(), idx.data_ptr(), stream, split=S,
+                               workspace=ws.data_ptr(), workspace_bytes=nbytes - 1)
+    assert rc == ds.DS_ERR_WORKSPACE

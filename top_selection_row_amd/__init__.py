@@ -1,0 +1,167 @@
+"""Python binding of the MI355X DeepSelect row-wise top-k library (``libdeepselect.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library. The functions named like the C ABI in ``include/deepselect.h`` take
+the same arguments (device pointers as integers, the stream as an integer
+``hipStream_t``); :func:`topk` is the torch-tensor convenience wrapper, which
+uses torch only to allocate outputs and to name the current stream.
+
+There is no fallback: if the library is missing or cannot load, importing the
+wrappers raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdeepselect.so")
+
+DS_F32, DS_BF16 = 0, 1
+DS_OK = 0
+DS_ERR_NULL, DS_ERR_DTYPE, DS_ERR_SHAPE, DS_ERR_K = -1, -2, -3, -4
+DS_ERR_BLOCK, DS_ERR_UNSUPPORTED, DS_ERR_HIP, DS_ERR_WORKSPACE = -5, -6, -7, -8
+DS_STATS_PER_ROW = 4
+STAT_NAMES = ("W", "A", "R", "max_len")
+
+EXPORTS = (
+    "deepselect_validate", "deepselect_topk", "deepselect_topk_ex", "deepselect_plan_split",
+    "deepselect_workspace_bytes", "deepselect_lds_bytes", "deepselect_status_string",
+    "deepselect_release",
+)
+
+
+class DsOptions(ctypes.Structure):
+    _fields_ = [("split", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("stats", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libdeepselect.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing; build it with `python -m top_selection_row_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp, u64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_uint64
+    lib.deepselect_validate.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32]
+    lib.deepselect_validate.restype = ctypes.c_int
+    lib.deepselect_topk.argtypes = [vp, ctypes.c_int, i64, i64, i64, i32, i32, i32, u64, vp, vp, vp]
+    lib.deepselect_topk.restype = ctypes.c_int
+    lib.deepselect_topk_ex.argtypes = [vp, ctypes.c_int, i64, i64, i64, i32, i32, i32, u64, vp, vp, vp,
+                                       ctypes.POINTER(DsOptions)]
+    lib.deepselect_topk_ex.restype = ctypes.c_int
+    lib.deepselect_plan_split.argtypes = [ctypes.c_int, i64, i64, i32, i32, i32, i32]
+    lib.deepselect_plan_split.restype = ctypes.c_int
+    lib.deepselect_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32, i32, i32, i32]
+    lib.deepselect_workspace_bytes.restype = ctypes.c_size_t
+    lib.deepselect_lds_bytes.argtypes = [ctypes.c_int, i64, i32, i32, i32, i32]
+    lib.deepselect_lds_bytes.restype = ctypes.c_size_t
+    lib.deepselect_status_string.argtypes = [ctypes.c_int]
+    lib.deepselect_status_string.restype = ctypes.c_char_p
+    lib.deepselect_release.argtypes = []
+    lib.deepselect_release.restype = None
+    _lib = lib
+    return lib
+
+
+class DeepSelectError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"deepselect status {status}: {deepselect_status_string(status)}")
+
+
+class DeepSelectArgumentError(DeepSelectError, ValueError):
+    pass
+
+
+def _check(status: int) -> int:
+    if status < 0:
+        if status in (DS_ERR_HIP,):
+            raise DeepSelectError(status)
+        raise DeepSelectArgumentError(status)
+    return status
+
+
+# ---------------------------------------------------------------- C-ABI names
+
+def deepselect_status_string(status: int) -> str:
+    return library().deepselect_status_string(int(status)).decode()
+
+
+def deepselect_validate(dtype, batch, n, row_stride, k, B, B2) -> int:
+    return library().deepselect_validate(dtype, batch, n, row_stride, k, B, B2)
+
+
+def deepselect_plan_split(dtype, batch, n, k, B, B2, num_cus) -> int:
+    return library().deepselect_plan_split(dtype, batch, n, k, B, B2, num_cus)
+
+
+def deepselect_workspace_bytes(dtype, batch, n, k, B, B2, split) -> int:
+    return library().deepselect_workspace_bytes(dtype, batch, n, k, B, B2, split)
+
+
+def deepselect_lds_bytes(dtype, n, k, B, B2, split) -> int:
+    return library().deepselect_lds_bytes(dtype, n, k, B, B2, split)
+
+
+def deepselect_release() -> None:
+    library().deepselect_release()
+
+
+def deepselect_topk(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals, out_idx, stream) -> int:
+    return library().deepselect_topk(x, dtype, batch, n, row_stride, k, B, B2, seed & (2**64 - 1),
+                                     out_vals, out_idx, stream)
+
+
+def deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals, out_idx, stream,
+                       split=0, stats=None, workspace=None, workspace_bytes=0) -> int:
+    opt = DsOptions(int(split), 0, stats, workspace, int(workspace_bytes))
+    return library().deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed & (2**64 - 1),
+                                        out_vals, out_idx, stream, ctypes.byref(opt))
+
+
+# ---------------------------------------------------------------- torch wrapper
+
+def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, stats: bool = False,
+         out=None, stream=None):
+    """Row-wise top-k of a 2-D CUDA tensor (float32 or bfloat16, unit column stride).
+
+    Returns (vals [batch, k] same dtype, idx [batch, k] int32) and, with
+    ``stats=True``, a [batch, 4] int64 tensor (W, A, R, max_len). The k entries
+    of a row are in no particular order. Raises on any rejected argument.
+    """
+    import torch
+
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D tensor with unit stride along the row")
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    if x.dtype == torch.float32:
+        dt = DS_F32
+    elif x.dtype == torch.bfloat16:
+        dt = DS_BF16
+    else:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    batch, n = x.shape
+    row_stride = x.stride(0) if batch > 1 else n
+    if out is None:
+        vals = torch.empty((batch, k), dtype=x.dtype, device=x.device)
+        idx = torch.empty((batch, k), dtype=torch.int32, device=x.device)
+    else:
+        vals, idx = out
+    st = torch.empty((batch, DS_STATS_PER_ROW), dtype=torch.int64, device=x.device) if stats else None
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        _check(deepselect_topk_ex(x.data_ptr(), dt, batch, n, row_stride, k, B, B2, seed,
+                                  vals.data_ptr(), idx.data_ptr(), stream, split=split,
+                                  stats=st.data_ptr() if st is not None else None))
+    if stats:
+        return vals, idx, st
+    return vals, idx
