@@ -31,8 +31,10 @@
  *     change before then. Nothing is copied device-to-host.
  *   - Every argument is checked on the host before any HIP call; a rejected call
  *     enqueues nothing. No C++ exception crosses this interface.
- *   - Entry points are thread-safe. Calls that share a library-owned workspace
- *     (same device and stream) are ordered by their stream.
+ *   - Entry points are thread-safe. The library-owned workspace of split rows
+ *     is kept per (device, stream), so calls sharing it are ordered by their
+ *     stream; it is allocated (hipMalloc) the first time a shape needs it and
+ *     grown when a later shape needs more.
  */
 #ifndef DEEPSELECT_H
 #define DEEPSELECT_H
@@ -75,13 +77,17 @@ typedef struct ds_options {
      * must satisfy 1 <= split <= ceil(N/B) and leave every part >= k elements,
      * else DS_ERR_BLOCK. */
     int32_t split;
-    int32_t reserved0;
+    /* Waves per workgroup of the streaming kernel: 0 = library choice, else 4
+     * or 8 (DS_ERR_BLOCK otherwise). Shapes the streaming kernel does not take
+     * (rows not 16-byte aligned, N*size or B*size not a multiple of 16, blocks
+     * over 8 KiB) run the generic 4-wave kernel whatever is asked. */
+    int32_t waves;
     /* Device pointer to batch*4 uint64 (layout above), or NULL for no statistics. */
     uint64_t *stats;
     /* Device workspace for split rows, or NULL for the library-owned one.
-     * Size from deepselect_workspace_bytes. A caller workspace must be
-     * zero-filled before its first use; every call leaves it zero-filled where
-     * that matters (its arrival counters reset themselves). */
+     * Size from deepselect_workspace_bytes; no initial contents are needed. It
+     * holds every part's k candidates between the part kernel and the merge
+     * kernel, so it must not be shared by calls that may overlap. */
     void *workspace;
     size_t workspace_bytes;
 } ds_options_t;

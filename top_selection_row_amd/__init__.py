@@ -32,7 +32,7 @@ EXPORTS = (
 
 
 class DsOptions(ctypes.Structure):
-    _fields_ = [("split", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+    _fields_ = [("split", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("stats", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t)]
 
@@ -120,16 +120,16 @@ def deepselect_topk(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals, ou
 
 
 def deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals, out_idx, stream,
-                       split=0, stats=None, workspace=None, workspace_bytes=0) -> int:
-    opt = DsOptions(int(split), 0, stats, workspace, int(workspace_bytes))
+                       split=0, stats=None, workspace=None, workspace_bytes=0, waves=0) -> int:
+    opt = DsOptions(int(split), int(waves), stats, workspace, int(workspace_bytes))
     return library().deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed & (2**64 - 1),
                                         out_vals, out_idx, stream, ctypes.byref(opt))
 
 
 # ---------------------------------------------------------------- torch wrapper
 
-def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, stats: bool = False,
-         out=None, stream=None):
+def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, waves: int = 0,
+         stats: bool = False, out=None, stream=None):
     """Row-wise top-k of a 2-D CUDA tensor (float32 or bfloat16, unit column stride).
 
     Returns (vals [batch, k] same dtype, idx [batch, k] int32) and, with
@@ -160,7 +160,7 @@ def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, stats: bo
         stream = torch.cuda.current_stream(x.device).cuda_stream
     with torch.cuda.device(x.device):
         _check(deepselect_topk_ex(x.data_ptr(), dt, batch, n, row_stride, k, B, B2, seed,
-                                  vals.data_ptr(), idx.data_ptr(), stream, split=split,
+                                  vals.data_ptr(), idx.data_ptr(), stream, split=split, waves=waves,
                                   stats=st.data_ptr() if st is not None else None))
     if stats:
         return vals, idx, st

@@ -1,28 +1,35 @@
 // deepselect.hip -- MI355X (gfx950) DeepSelect batched row-wise top-k and its C ABI.
 //
 // DeepSelect (DeepSelect deep-dive, PFCCLab/DeepSelect, section "算法"): each row
-// is read once, in B-element blocks taken in a random order independent of the
-// data. Elements above the threshold T go to an on-chip candidate buffer; when
-// the buffer reaches k + B2 entries a radix select keeps its k largest and T
-// becomes the k-th. A final select returns k. Before the first compaction every
-// element is admitted (the page says so right after the pseudo-code).
+// is read once, in B-element blocks taken in a random order that does not
+// depend on the data. Elements above the threshold T go to an on-chip candidate
+// buffer; after any block that leaves k + B2 or more entries, a radix select
+// keeps the k largest and T becomes the k-th. A final select returns k. Before
+// the first compaction every element is admitted (the page says so right after
+// the pseudo-code).
 //
 // Mapping on gfx950
-//   * one 256-lane workgroup per (row, part); the candidate buffer (keys + column
-//     indices), the radix histograms and the block order live in LDS;
-//   * a block is streamed as 4 KiB tiles, one 16-byte buffer load per lane, kept
-//     P tiles ahead in a register ring (the block order is known up front, so
-//     loads never wait on the filter); lanes past the end of a block get an
-//     out-of-range buffer offset, which returns zero and touches no memory;
-//   * the filter compares raw bits against the threshold (signed compare when
-//     T >= +0, unsigned "less than" when T < 0, both exact under the key order)
-//     and compacts survivors with 64-bit ballot masks, mbcnt ranks and one
-//     4-wave prefix through LDS;
+//   * one workgroup per (row, part) owns the candidate buffer (keys + column
+//     indices), the radix histograms and the block order in LDS;
+//   * streaming kernel: each wave owns whole blocks. A step hands the next NW
+//     blocks of the order to the NW waves; each lane holds its share of its
+//     block in registers (U 16-byte buffer loads) while the wave counts the
+//     elements above T with 64-bit ballots. One barrier exchanges the NW counts,
+//     after which every wave knows where its survivors go and whether some
+//     block of the step ends with the buffer at k + B2 or more. If so, the
+//     buffer is compacted right after that block and the later blocks of the
+//     step are counted again against the new T, so the result and every
+//     statistic are those of the block-by-block loop of the pages. Loads run P
+//     steps ahead of use; lanes past the end of a block get an out-of-range
+//     buffer offset, which returns zero and touches no memory;
+//   * generic kernel (unaligned rows, ragged N, blocks over 8 KiB): the whole
+//     workgroup shares each block, one barrier per 4 KiB tile;
 //   * split rows (the deep-dive's "实现" section, last paragraph: a row cut into
 //     parts whose top-k go to one reducer): each part writes its k results to a
-//     device workspace, publishes them with an agent-scope release and an
-//     arrival counter, and the last part to arrive runs DeepSelect once more
-//     over the parts' results (one block per part) and writes the row.
+//     device workspace; a second kernel, queued behind the first on the same
+//     stream, runs DeepSelect over the parts' results (one block per part) and
+//     writes the row. The kernel boundary makes the parts' writes visible, so
+//     no device-wide fence or arrival counter is needed.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -45,22 +52,22 @@ struct Params {
     void* out_vals;
     int32_t* out_idx;
     uint64_t* stats;
-    uint32_t* ws_arrive;
     uint32_t* ws_keys;
     uint32_t* ws_idx;
     uint64_t* ws_stats;
     int64_t batch, n, row_stride, m;
     uint64_t seed;
-    int32_t k, B, B2, split, tpb;
+    int32_t k, B, B2, split;
     Layout L;
 };
 
 struct RunState {
-    uint32_t len = 0;      // candidate entries
-    bool tset = false;     // threshold set (a compaction happened)
-    uint32_t tkey = 0;     // threshold key
-    uint64_t W = 0, A = 0, R = 0, maxlen = 0;
-    uint32_t par = 0;      // count-buffer parity
+    uint32_t len = 0;   // candidate entries
+    bool tset = false;  // threshold set (a compaction happened)
+    uint32_t tkey = 0;  // threshold key
+    uint64_t W = 0;     // RadixSelectTopK input (can pass 2^32 for huge k / tiny B2)
+    uint32_t A = 0, R = 0, maxlen = 0;
+    uint32_t par = 0;   // count-buffer parity
 };
 
 template <class D>
@@ -69,9 +76,10 @@ struct Lds {
     uint32_t* idx;
     uint32_t* cnt;
     uint16_t* perm;
-    uint32_t* misc;
+    uint32_t* misc;  // [0] broadcast flag, [1] largest key appended so far
     SelectScratch sc;
     unsigned char* base;
+    Layout L;
 };
 
 template <class D>
@@ -85,300 +93,295 @@ __device__ __forceinline__ Lds<D> lds_of(unsigned char* smem, const Layout& L) {
     s.misc = reinterpret_cast<uint32_t*>(smem + L.misc);
     s.sc.hist = reinterpret_cast<uint32_t*>(smem + L.hist);
     s.sc.pcnt = reinterpret_cast<uint32_t*>(smem + L.pcnt);
-    s.sc.hset = 0;
+    s.L = L;
     return s;
 }
 
-// RadixSelectTopK kept out of line so one copy serves every unrolled ring
-// slot. Arguments and result travel by value (k-th key in the low word, the
-// clean histogram set in the high word) so nothing lives in scratch memory.
-template <class D>
-__device__ __noinline__ uint64_t compact_call(typename D::Key* keys, uint32_t* idx, uint32_t* hist,
-                                              uint32_t* pcnt, uint32_t n, uint32_t k, uint32_t hset) {
-    SelectScratch sc{hist, pcnt, hset};
-    const uint32_t kth = radix_select<D>(keys, idx, n, k, sc);
-    return ((uint64_t)sc.hset << 32) | kth;
+// Fold this wave's largest appended key into misc[1] (used to skip radix
+// digits that every candidate shares).
+__device__ __forceinline__ void publish_max(uint32_t* misc, uint32_t kmax) {
+    kmax = wave_max(kmax);
+    if (lane_id() == 0 && kmax != 0u) atomicMax(&misc[1], kmax);
 }
 
-// Compaction after a block: RadixSelectTopK(buffer, k), T = k-th key.
-template <class D>
-__device__ __forceinline__ void maybe_compact(Lds<D>& s, RunState& st, uint32_t k, uint32_t B2) {
-    st.maxlen = st.len > st.maxlen ? st.len : st.maxlen;
-    if (st.len >= k + B2) {
-        st.W += st.len;
-        st.R += 1;
-        const uint64_t r = compact_call<D>(s.keys, s.idx, s.sc.hist, s.sc.pcnt, st.len, k, s.sc.hset);
-        st.tkey = (uint32_t)r;
-        s.sc.hset = (uint32_t)(r >> 32);
-        st.tset = true;
-        st.len = k;
-    }
+// RadixSelectTopK kept out of line so one copy serves every unrolled slot.
+// Arguments and result travel by value so nothing lives in scratch memory, and
+// the LDS arrays are rebuilt here from the workgroup's LDS base and their byte
+// offsets: a pointer passed across the call would lose its address space and
+// turn every access into a flat access.
+template <class D, int NW>
+__device__ __noinline__ uint32_t compact_call(uint32_t keys_off, uint32_t idx_off, uint32_t hist_off,
+                                              uint32_t pcnt_off, uint32_t misc_off, uint32_t n, uint32_t k,
+                                              uint32_t lo_key) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    SelectScratch sc{reinterpret_cast<uint32_t*>(smem + hist_off), reinterpret_cast<uint32_t*>(smem + pcnt_off)};
+    return radix_select<D, NW>(reinterpret_cast<typename D::Key*>(smem + keys_off),
+                               reinterpret_cast<uint32_t*>(smem + idx_off), n, k, sc, lo_key,
+                               reinterpret_cast<const uint32_t*>(smem + misc_off) + 1);
 }
 
-// ---------------------------------------------------------------------------
-// Raw row source: tiles of 256 lanes x 16 bytes.
-// ---------------------------------------------------------------------------
-template <class D, bool kVec>
-struct RowTiles {
-    static constexpr int kPer = D::kPerLoad;           // elements per lane per tile
-    static constexpr int kTE = kWG * kPer;              // elements per tile
-    using Reg = u32x4;                                  // kVec: one 16-byte load
-    struct Ring {
-        u32x4 v[kVec ? 1 : (kPer + 3) / 4];
-    };
-};
-
-template <class D, bool kVec>
-__device__ __forceinline__ void load_tile(typename RowTiles<D, kVec>::Ring& r, __amdgpu_buffer_rsrc_t rsrc,
-                                          int64_t elem_off, int32_t tv) {
-    constexpr int kPer = D::kPerLoad;
-    const int lane = threadIdx.x;
-    if constexpr (kVec) {
-        const bool ok = (lane + 1) * kPer <= tv;
-        const uint32_t off = ok ? (uint32_t)((elem_off + (int64_t)lane * kPer) * D::kBytes) : kOob;
-        r.v[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
-    } else {
-#pragma unroll
-        for (int s = 0; s < kPer; ++s) {
-            const int e = s * kWG + lane;
-            const uint32_t off = e < tv ? (uint32_t)((elem_off + e) * D::kBytes) : kOob;
-            uint32_t val;
-            if constexpr (D::kBytes == 4)
-                val = __builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0);
-            else
-                val = __builtin_amdgcn_raw_buffer_load_b16(rsrc, off, 0, 0);
-            r.v[s / 4][s % 4] = val;
-        }
-    }
+template <class D, int NW>
+__device__ __forceinline__ uint32_t select_call(Lds<D>& s, uint32_t n, uint32_t k, uint32_t lo_key) {
+    return compact_call<D, NW>(s.L.keys, s.L.idx, s.L.hist, s.L.pcnt, s.L.misc, n, k, lo_key);
 }
 
-// Raw pattern of slot s of this lane's part of a tile, and its element offset
-// inside the tile.
-template <class D, bool kVec>
-__device__ __forceinline__ uint32_t slot_raw(const typename RowTiles<D, kVec>::Ring& r, int s) {
-    if constexpr (kVec && D::kBytes == 2) {
-        const uint32_t w = r.v[0][s >> 1];
-        return (s & 1) ? (w >> 16) : (w & 0xFFFFu);
-    } else {
-        return r.v[s / 4][s % 4];
-    }
-}
-template <class D, bool kVec>
-__device__ __forceinline__ int slot_elem(int s) {
-    if constexpr (kVec)
-        return (int)threadIdx.x * D::kPerLoad + s;
-    else
-        return s * kWG + (int)threadIdx.x;
+// Compaction: RadixSelectTopK(buffer, k), T = k-th key. Keys are >= T once T
+// is set, which bounds the radix digits from below.
+template <class D, int NW>
+__device__ __forceinline__ void compact(Lds<D>& s, RunState& st, uint32_t k) {
+    st.W += st.len;
+    st.R += 1;
+    st.tkey = select_call<D, NW>(s, st.len, k, st.tset ? st.tkey : 0u);
+    st.tset = true;
+    st.len = k;
 }
 
-// Filter predicate of slot s against threshold constants (T set).
-// f32: neg ? raw < traw (unsigned) : (int)raw > (int)traw.
-// bf16 (raw in the top half of a 32-bit word): neg ? w < thr : (int)w > (int)thr
-// with thr = traw<<16 (neg) or traw<<16 | 0xFFFF.
-template <class D, bool kVec>
-__device__ __forceinline__ bool slot_pass(const typename RowTiles<D, kVec>::Ring& r, int s, bool neg,
-                                          uint32_t thr) {
-    if constexpr (D::kBytes == 4) {
-        const uint32_t u = r.v[s / 4][s % 4];
-        return neg ? (u < thr) : ((int32_t)u > (int32_t)thr);
-    } else {
-        uint32_t w;
-        if constexpr (kVec) {
-            const uint32_t d = r.v[0][s >> 1];
-            w = (s & 1) ? d : (d << 16);
-        } else {
-            w = r.v[s / 4][s % 4] << 16;
-        }
-        return neg ? (w < thr) : ((int32_t)w > (int32_t)thr);
-    }
-}
-
-template <class D>
-__device__ __forceinline__ void threshold_consts(const RunState& st, bool& neg, uint32_t& thr) {
-    if constexpr (D::kBytes == 4) {
-        neg = st.tkey < 0x80000000u;
-        thr = D::raw(st.tkey);
-    } else {
-        neg = st.tkey < 0x8000u;
-        const uint32_t t = D::raw(st.tkey) << 16;
-        thr = neg ? t : (t | 0xFFFFu);
-    }
-}
-
-// Process one tile: admit-all before the first compaction, else filter.
-template <class D, bool kVec>
-__device__ __forceinline__ void process_tile(Lds<D>& s, RunState& st, const typename RowTiles<D, kVec>::Ring& r,
-                                             int64_t elem_base, int32_t tv) {
-    constexpr int kPer = D::kPerLoad;
-    if (tv <= 0) return;
-    if (!st.tset) {
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-            const int e = slot_elem<D, kVec>(q);
-            if (e < tv) {
-                const uint32_t pos = st.len + (uint32_t)e;
-                s.keys[pos] = (typename D::Key)D::key(slot_raw<D, kVec>(r, q));
-                s.idx[pos] = (uint32_t)(elem_base + e);
-            }
-        }
-        st.len += (uint32_t)tv;
-        st.A += (uint32_t)tv;
-        return;
-    }
-    bool neg;
-    uint32_t thr;
-    threshold_consts<D>(st, neg, thr);
-    bool pred[kPer];
-    uint64_t masks[kPer];
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-        const bool inb = kVec ? true : (slot_elem<D, kVec>(q) < tv);
-        // vector tiles: lanes past tv loaded zeros; exclude them explicitly
-        const bool valid = kVec ? ((int)threadIdx.x * kPer < tv) : inb;
-        pred[q] = valid && slot_pass<D, kVec>(r, q, neg, thr);
-        masks[q] = __ballot(pred[q]);
-    }
-    const uint32_t added = append_masked<kPer>(masks, pred, st.len, s.cnt, st.par, [&](int q, uint32_t pos) {
-        s.keys[pos] = (typename D::Key)D::key(slot_raw<D, kVec>(r, q));
-        s.idx[pos] = (uint32_t)(elem_base + slot_elem<D, kVec>(q));
-    });
-    st.len += added;
-    st.A += added;
-}
-
-// Stream the blocks of one part in the random order in s.perm.
-template <class D, bool kVec, int P>
-__device__ void stream_part(Lds<D>& s, RunState& st, const Params& p, __amdgpu_buffer_rsrc_t rsrc,
-                            int64_t part_elem0, int64_t part_n, int32_t ms) {
-    using Ring = typename RowTiles<D, kVec>::Ring;
-    constexpr int kTE = RowTiles<D, kVec>::kTE;
-    const int32_t tpb = p.tpb;
-    const int64_t B = p.B;
-    const int32_t ntiles = ms * tpb;
-    const uint32_t k = (uint32_t)p.k, B2 = (uint32_t)p.B2;
-
-    // load-side cursor
-    int32_t lblk = 0, lsub = 0;
-    auto tile_geom = [&](int32_t bi, int32_t sub, int64_t& off, int32_t& tv) {
-        if (bi >= ms) {
-            off = 0;
-            tv = 0;
-            return;
-        }
-        const int64_t b = (int64_t)uniform(s.perm[bi]);
-        const int64_t blen = (b * B + B <= part_n) ? B : (part_n - b * B);
-        const int64_t rem = blen - (int64_t)sub * kTE;
-        tv = (int32_t)(rem < kTE ? (rem > 0 ? rem : 0) : kTE);
-        off = b * B + (int64_t)sub * kTE;
-    };
-    auto advance = [&](int32_t& bi, int32_t& sub) {
-        if (++sub == tpb) {
-            sub = 0;
-            ++bi;
-        }
-    };
-
-    Ring ring[P];
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-        int64_t off;
-        int32_t tv;
-        tile_geom(lblk, lsub, off, tv);
-        load_tile<D, kVec>(ring[j], rsrc, off, tv);
-        advance(lblk, lsub);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    int32_t pblk = 0, psub = 0;
-    for (int32_t t0 = 0; t0 < ntiles; t0 += P) {
-#pragma unroll
-        for (int j = 0; j < P; ++j) {
-            if (t0 + j < ntiles) {
-                int64_t off;
-                int32_t tv;
-                tile_geom(pblk, psub, off, tv);
-                process_tile<D, kVec>(s, st, ring[j], part_elem0 + off, tv);
-                if (psub == tpb - 1) maybe_compact<D>(s, st, k, B2);
-                advance(pblk, psub);
-            }
-            int64_t off;
-            int32_t tv;
-            tile_geom(lblk, lsub, off, tv);
-            load_tile<D, kVec>(ring[j], rsrc, off, tv);
-            advance(lblk, lsub);
-        }
-    }
-}
-
-// Final RadixSelectTopK (its input length counts in W).
-template <class D>
+// Final RadixSelectTopK (its input length counts in W); ends with a barrier.
+template <class D, int NW>
 __device__ __forceinline__ void final_select(Lds<D>& s, RunState& st, uint32_t k) {
     st.W += st.len;
     if (st.len > k) {
-        st.tkey = radix_select<D>(s.keys, s.idx, st.len, k, s.sc);
+        st.tkey = select_call<D, NW>(s, st.len, k, st.tset ? st.tkey : 0u);
         st.len = k;
     }
     __syncthreads();
 }
 
-// Merge of split rows: DeepSelect over the parts' results, one block per part.
-template <class D>
-__device__ void merge_parts(Lds<D>& s, RunState& st, const Params& p, int64_t row) {
-    const uint32_t k = (uint32_t)p.k, B2 = (uint32_t)p.B2;
-    const int32_t S = p.split;
-    build_order(s.perm, p.seed, row, 1, 0, S, s.base);
-    for (int32_t i = 0; i < S; ++i) {
-        const int64_t part = (int64_t)uniform(s.perm[i]);
-        const uint32_t* wk = p.ws_keys + (row * S + part) * (int64_t)k;
-        const uint32_t* wi = p.ws_idx + (row * S + part) * (int64_t)k;
-        for (uint32_t t0 = 0; t0 < k; t0 += kWG * 4) {
-            const uint32_t tv = (k - t0) < (uint32_t)(kWG * 4) ? (k - t0) : (uint32_t)(kWG * 4);
-            uint32_t kk[4], ii[4];
-            bool inb[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t e = (uint32_t)threadIdx.x * 4u + (uint32_t)q;
-                inb[q] = e < tv;
-                kk[q] = inb[q] ? __builtin_nontemporal_load(wk + t0 + e) : 0u;
-                ii[q] = inb[q] ? __builtin_nontemporal_load(wi + t0 + e) : 0u;
-            }
-            if (!st.tset) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (inb[q]) {
-                        const uint32_t pos = st.len + (uint32_t)threadIdx.x * 4u + (uint32_t)q;
-                        s.keys[pos] = (typename D::Key)kk[q];
-                        s.idx[pos] = ii[q];
-                    }
-                }
-                st.len += tv;
-                st.A += tv;
-            } else {
-                bool pred[4];
-                uint64_t masks[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    pred[q] = inb[q] && kk[q] > st.tkey;
-                    masks[q] = __ballot(pred[q]);
-                }
-                const uint32_t added = append_masked<4>(masks, pred, st.len, s.cnt, st.par,
-                                                        [&](int q, uint32_t pos) {
-                                                            s.keys[pos] = (typename D::Key)kk[q];
-                                                            s.idx[pos] = ii[q];
-                                                        });
-                st.len += added;
-                st.A += added;
-            }
-        }
-        maybe_compact<D>(s, st, k, B2);
+// ===========================================================================
+// Streaming kernel: each wave owns whole blocks of U units (one 16-byte load
+// per lane per unit; a unit is 64*V elements, V = elements per 16 bytes).
+// ===========================================================================
+template <int U>
+struct BlockRegs {
+    u32x4 v[U];
+};
+
+// Raw bits of slot q of unit u, and the 32-bit word the threshold test reads
+// (bfloat16: the pattern moved to the top half).
+template <class D, int U>
+__device__ __forceinline__ uint32_t raw_at(const BlockRegs<U>& r, int u, int q) {
+    if constexpr (D::kBytes == 4) {
+        return r.v[u][q];
+    } else {
+        const uint32_t d = r.v[u][q >> 1];
+        return (q & 1) ? (d >> 16) : (d & 0xFFFFu);
     }
-    final_select<D>(s, st, k);
+}
+template <class D, int U>
+__device__ __forceinline__ uint32_t test_word(const BlockRegs<U>& r, int u, int q) {
+    if constexpr (D::kBytes == 4) {
+        return r.v[u][q];
+    } else {
+        const uint32_t d = r.v[u][q >> 1];
+        return (q & 1) ? d : (d << 16);
+    }
 }
 
-template <class D>
-__device__ __forceinline__ void write_row(Lds<D>& s, const RunState& st, const Params& p, int64_t row,
-                                          uint64_t W, uint64_t A, uint64_t R, uint64_t maxlen) {
+template <class D, int NW, int U, int P>
+struct Streamer {
+    static constexpr int V = D::kPerLoad;
+    static constexpr int UE = 64 * V;  // elements per unit
+
+    Lds<D>& s;
+    RunState& st;
+    const __amdgpu_buffer_rsrc_t rsrc;
+    const uint32_t part_elem0, part_n, B;  // parts hold < 2^31 bytes
+    const int32_t ms, nsteps;
+    const uint32_t k, B2;
+
+    // Block at order position bi: element offset inside the part and length.
+    __device__ __forceinline__ void block_at(int32_t bi, uint32_t& boff, uint32_t& blen) const {
+        if (bi >= ms) {
+            boff = 0;
+            blen = 0;
+            return;
+        }
+        boff = uniform(s.perm[bi]) * B;
+        const uint32_t rem = part_n - boff;
+        blen = rem < B ? rem : B;
+    }
+
+    __device__ __forceinline__ void load(BlockRegs<U>& r, int32_t bi) const {
+        uint32_t boff, blen;
+        block_at(bi, boff, blen);
+        const uint32_t lane = lane_id();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t e0 = u * UE + lane * V;
+            const uint32_t off = e0 + V <= blen ? (boff + e0) * D::kBytes : kOob;
+            r.v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+        }
+    }
+
+    // Lanes past the end of a short block read zeros; give them all-ones bits
+    // instead, whose key is 0: never above any threshold.
+    __device__ __forceinline__ void mask_tail(BlockRegs<U>& r, uint32_t blen) const {
+        const uint32_t lane = lane_id();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u * UE + lane * V >= blen) r.v[u] = u32x4{~0u, ~0u, ~0u, ~0u};
+        }
+    }
+
+    // Elements of this wave's block above T (uniform over the wave).
+    template <bool kNeg>
+    __device__ __forceinline__ uint32_t count_above(const BlockRegs<U>& r, uint32_t thr) const {
+        uint32_t c = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int q = 0; q < V; ++q) c += (uint32_t)__popcll(__ballot(above_k<kNeg>(test_word<D, U>(r, u, q), thr)));
+        }
+        return c;
+    }
+
+    // Append every element of this wave's block at base (before the first
+    // compaction), in element order.
+    __device__ __forceinline__ void scatter_all(const BlockRegs<U>& r, uint32_t base, uint32_t boff,
+                                                uint32_t blen) const {
+        const uint32_t lane = lane_id();
+        const uint32_t col0 = part_elem0 + boff;
+        uint32_t kmax = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int q = 0; q < V; ++q) {
+                const uint32_t e = u * UE + lane * V + q;
+                if (e < blen) {
+                    const uint32_t key = D::key(raw_at<D, U>(r, u, q));
+                    s.keys[base + e] = (typename D::Key)key;
+                    s.idx[base + e] = col0 + e;
+                    kmax = key > kmax ? key : kmax;
+                }
+            }
+        }
+        publish_max(s.misc, kmax);
+    }
+
+    // Append the elements of this wave's block above T at base, in (unit,
+    // slot, lane) order.
+    template <bool kNeg>
+    __device__ __forceinline__ void scatter_above(const BlockRegs<U>& r, uint32_t base, uint32_t boff,
+                                                  uint32_t thr) const {
+        const uint32_t col0 = part_elem0 + boff + lane_id() * V;
+        uint32_t kmax = 0, off = base;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int q = 0; q < V; ++q) {
+                const bool pred = above_k<kNeg>(test_word<D, U>(r, u, q), thr);
+                const uint64_t m = __ballot(pred);
+                if (m != 0ull) {
+                    if (pred) {
+                        const uint32_t pos = off + lanes_below(m);
+                        const uint32_t key = D::key(raw_at<D, U>(r, u, q));
+                        s.keys[pos] = (typename D::Key)key;
+                        s.idx[pos] = col0 + (uint32_t)(u * UE + q);
+                        kmax = key > kmax ? key : kmax;
+                    }
+                    off += (uint32_t)__popcll(m);
+                }
+            }
+        }
+        publish_max(s.misc, kmax);
+    }
+
+    // Count this wave's block against the current state (every element while
+    // the threshold is unset).
+    __device__ __forceinline__ uint32_t count_block(const BlockRegs<U>& r, uint32_t blen) const {
+        if (!st.tset) return blen;
+        const Thresh th = make_thresh<D>(st.tkey);
+        return th.neg ? count_above<true>(r, th.thr) : count_above<false>(r, th.thr);
+    }
+
+    __device__ __forceinline__ void scatter_block(const BlockRegs<U>& r, uint32_t base, uint32_t boff,
+                                                  uint32_t blen) const {
+        if (!st.tset) {
+            scatter_all(r, base, boff, blen);
+        } else {
+            const Thresh th = make_thresh<D>(st.tkey);
+            if (th.neg)
+                scatter_above<true>(r, base, boff, th.thr);
+            else
+                scatter_above<false>(r, base, boff, th.thr);
+        }
+    }
+
+    // Blocks first..nblk-1 of the step, counted against the current state:
+    // publish the counts, then append them in order up to (and including) the
+    // first block after which the buffer holds k + B2 or more. Returns that
+    // block's wave, or -1 when every block was appended without reaching it.
+    __device__ __forceinline__ int32_t append_from(const BlockRegs<U>& r, uint32_t boff, uint32_t blen,
+                                                   int32_t first, int32_t nblk) {
+        const int w = wave_id();
+        const bool mine = w >= first && w < nblk;
+        const uint32_t c = mine ? count_block(r, blen) : 0u;
+        if (lane_id() == 0) s.cnt[st.par * NW + w] = c;
+        __syncthreads();
+        uint32_t cs[NW];
+#pragma unroll
+        for (int g = 0; g < NW; ++g) cs[g] = uniform(s.cnt[st.par * NW + g]);
+        st.par ^= 1u;
+        // the pages' order: block after block, compaction check after each
+        uint32_t run = st.len, my_base = 0;
+        int32_t trig = -1;
+#pragma unroll
+        for (int g = 0; g < NW; ++g) {
+            if (g >= first && g < nblk && trig < 0) {
+                if (g == w) my_base = run;
+                run += cs[g];
+                if (run >= k + B2) trig = g;
+            }
+        }
+        const int32_t last = trig >= 0 ? trig : nblk - 1;
+        if (mine && w <= last && c != 0) scatter_block(r, my_base, boff, blen);
+        st.A += run - st.len;
+        st.maxlen = run > st.maxlen ? run : st.maxlen;
+        st.len = run;
+        return trig;
+    }
+
+    // One step: the blocks at order positions step*NW + w, w = 0..NW-1. The
+    // common case (no compaction inside the step) is straight-line code; after
+    // a compaction the blocks behind it are counted again against the new T.
+    __device__ __forceinline__ void step(BlockRegs<U>& r, int32_t stp) {
+        uint32_t boff, blen;
+        block_at(stp * NW + wave_id(), boff, blen);
+        if (blen != U * UE) mask_tail(r, blen);
+        const int32_t nblk = ms - stp * NW < NW ? ms - stp * NW : NW;  // blocks in this step
+        int32_t trig = append_from(r, boff, blen, 0, nblk);
+        if (trig >= 0) {
+            compact<D, NW>(s, st, k);
+            while (trig >= 0 && trig < nblk - 1) {
+                trig = append_from(r, boff, blen, trig + 1, nblk);
+                if (trig >= 0) compact<D, NW>(s, st, k);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void run() {
+        const int w = wave_id();
+        BlockRegs<U> ring[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            load(ring[j], j * NW + w);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int32_t s0 = 0; s0 < nsteps; s0 += P) {
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                if (s0 + j < nsteps) step(ring[j], s0 + j);
+                load(ring[j], (s0 + j + P) * NW + w);
+            }
+        }
+    }
+};
+
+template <class D, int NW>
+__device__ __forceinline__ void write_row(Lds<D>& s, const Params& p, int64_t row, uint64_t W, uint64_t A,
+                                          uint64_t R, uint64_t maxlen) {
     const int64_t k = p.k;
-    for (int64_t j = threadIdx.x; j < k; j += kWG) {
+    for (int64_t j = threadIdx.x; j < k; j += NW * 64) {
         const uint32_t key = s.keys[j];
         if constexpr (D::kBytes == 4)
             reinterpret_cast<uint32_t*>(p.out_vals)[row * k + j] = D::raw(key);
@@ -395,84 +398,340 @@ __device__ __forceinline__ void write_row(Lds<D>& s, const RunState& st, const P
     }
 }
 
-template <class D, bool kVec, int P>
-__global__ __launch_bounds__(kWG) void deepselect_kernel(Params p) {
+// Part results of split rows go to the workspace for the merge kernel.
+template <class D, int NW>
+__device__ __forceinline__ void write_part(Lds<D>& s, const RunState& st, const Params& p, int64_t slot) {
+    for (int64_t j = threadIdx.x; j < p.k; j += NW * 64) {
+        p.ws_keys[slot * p.k + j] = (uint32_t)s.keys[j];
+        p.ws_idx[slot * p.k + j] = s.idx[j];
+    }
+    if (threadIdx.x == 0) {
+        uint64_t* o = p.ws_stats + slot * DS_STATS_PER_ROW;
+        o[DS_STAT_W] = st.W;
+        o[DS_STAT_A] = st.A;
+        o[DS_STAT_R] = st.R;
+        o[DS_STAT_MAX_LEN] = st.maxlen;
+    }
+}
+
+struct PartGeom {
+    int64_t row, slot, b0, part_elem0, part_n;
+    int32_t part, ms;
+};
+
+__device__ __forceinline__ PartGeom part_geom(const Params& p, int64_t item) {
+    PartGeom g;
+    g.row = item / p.split;
+    g.part = (int32_t)(item % p.split);
+    g.slot = item;
+    g.b0 = part_begin(p.m, g.part, p.split);
+    const int64_t b1 = part_begin(p.m, g.part + 1, p.split);
+    g.ms = (int32_t)(b1 - g.b0);
+    g.part_elem0 = g.b0 * (int64_t)p.B;
+    g.part_n = ((b1 * (int64_t)p.B < p.n) ? b1 * (int64_t)p.B : p.n) - g.part_elem0;
+    return g;
+}
+
+template <class D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const Params& p, const PartGeom& g) {
+    const unsigned char* rowp =
+        reinterpret_cast<const unsigned char*>(p.x) + (g.row * p.row_stride + g.part_elem0) * D::kBytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(rowp), (short)0,
+                                             (int)(g.part_n * D::kBytes), (int)kRsrcWord3);
+}
+
+template <class D, int NW, int U, int P>
+__global__ __launch_bounds__(NW * 64) void deepselect_stream_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     Lds<D> s = lds_of<D>(smem, p.L);
     const int64_t items = p.batch * (int64_t)p.split;
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-        const int64_t row = item / p.split;
-        const int32_t part = (int32_t)(item % p.split);
+        const PartGeom g = part_geom(p, item);
         __syncthreads();  // LDS free from the previous item
-        zero_hist(s.sc);
-
-        const int64_t b0 = part_begin(p.m, part, p.split), b1 = part_begin(p.m, part + 1, p.split);
-        const int32_t ms = (int32_t)(b1 - b0);
-        const int64_t part_elem0 = b0 * (int64_t)p.B;
-        const int64_t part_n = ((b1 * (int64_t)p.B < p.n) ? b1 * (int64_t)p.B : p.n) - part_elem0;
-        const unsigned char* rowp = reinterpret_cast<const unsigned char*>(p.x) +
-                                    (row * p.row_stride + part_elem0) * D::kBytes;
-        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<unsigned char*>(rowp), (short)0, (int)(part_n * D::kBytes), (int)kRsrcWord3);
-
-        build_order(s.perm, p.seed, row, 0, b0, ms, s.base);
+        clear_hist<NW>(s.sc.hist);
+        if (threadIdx.x == 0) s.misc[1] = 0u;
+        build_order<NW>(s.perm, p.seed, g.row, 0, g.b0, g.ms, s.base);
         RunState st;
-        stream_part<D, kVec, P>(s, st, p, rsrc, part_elem0, part_n, ms);
-        final_select<D>(s, st, (uint32_t)p.k);
-
-        if (p.split == 1) {
-            write_row<D>(s, st, p, row, st.W, st.A, st.R, st.maxlen);
-            continue;
-        }
-        // publish this part's k results and statistics
-        const int64_t slot = row * p.split + part;
-        for (int64_t j = threadIdx.x; j < p.k; j += kWG) {
-            p.ws_keys[slot * p.k + j] = (uint32_t)s.keys[j];
-            p.ws_idx[slot * p.k + j] = s.idx[j];
-        }
-        if (threadIdx.x == 0) {
-            uint64_t* o = p.ws_stats + slot * DS_STATS_PER_ROW;
-            o[DS_STAT_W] = st.W;
-            o[DS_STAT_A] = st.A;
-            o[DS_STAT_R] = st.R;
-            o[DS_STAT_MAX_LEN] = st.maxlen;
-        }
-        __threadfence();  // release: this thread's stores are visible device-wide
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t old = atomicAdd(p.ws_arrive + row, 1u);
-            s.misc[0] = (old == (uint32_t)p.split - 1u) ? 1u : 0u;
-        }
-        __syncthreads();
-        if (s.misc[0] == 0u) continue;
-        __threadfence();  // acquire: the other parts' stores are visible here
-        if (threadIdx.x == 0) p.ws_arrive[row] = 0u;  // ready for the next call
-
-        uint64_t W = 0, A = 0, R = 0, maxlen = 0;
-        for (int32_t q = 0; q < p.split; ++q) {
-            const uint64_t* o = p.ws_stats + (row * p.split + q) * DS_STATS_PER_ROW;
-            W += __builtin_nontemporal_load(o + DS_STAT_W);
-            A += __builtin_nontemporal_load(o + DS_STAT_A);
-            R += __builtin_nontemporal_load(o + DS_STAT_R);
-            const uint64_t ml = __builtin_nontemporal_load(o + DS_STAT_MAX_LEN);
-            maxlen = ml > maxlen ? ml : maxlen;
-        }
-        __syncthreads();  // everyone is done with the part's buffer
-        RunState mst;
-        merge_parts<D>(s, mst, p, row);
-        write_row<D>(s, mst, p, row, W + mst.W, A + mst.A, R + mst.R,
-                     mst.maxlen > maxlen ? mst.maxlen : maxlen);
+        Streamer<D, NW, U, P> sm{s,
+                                 st,
+                                 part_rsrc<D>(p, g),
+                                 (uint32_t)g.part_elem0,
+                                 (uint32_t)g.part_n,
+                                 (uint32_t)p.B,
+                                 g.ms,
+                                 (int32_t)ceil_div(g.ms, NW),
+                                 (uint32_t)p.k,
+                                 (uint32_t)p.B2};
+        sm.run();
+        final_select<D, NW>(s, st, (uint32_t)p.k);
+        if (p.split == 1)
+            write_row<D, NW>(s, p, g.row, st.W, st.A, st.R, st.maxlen);
+        else
+            write_part<D, NW>(s, st, p, g.slot);
     }
 }
 
-__global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
+// ===========================================================================
+// Generic kernel: the whole workgroup shares each block; a tile is one 16-byte
+// load (or V scalar loads) per lane, one barrier per tile. Any alignment, any N,
+// any block size.
+// ===========================================================================
+constexpr int kGW = 4;  // waves of the generic and merge kernels
+
+template <class D, bool kVec>
+struct TileRegs {
+    u32x4 v[kVec ? 1 : (D::kPerLoad + 3) / 4];
+};
+
+template <class D, bool kVec>
+__device__ __forceinline__ int tile_elem(int q) {
+    if constexpr (kVec)
+        return (int)threadIdx.x * D::kPerLoad + q;
+    else
+        return q * kGW * 64 + (int)threadIdx.x;
 }
 
-// ---------------------------------------------------------------------------
+template <class D, bool kVec>
+__device__ __forceinline__ void load_tile(TileRegs<D, kVec>& r, __amdgpu_buffer_rsrc_t rsrc, int64_t elem_off,
+                                          int32_t tv) {
+    constexpr int V = D::kPerLoad;
+    if constexpr (kVec) {
+        const bool ok = ((int)threadIdx.x + 1) * V <= tv;
+        const uint32_t off = ok ? (uint32_t)((elem_off + (int64_t)threadIdx.x * V) * D::kBytes) : kOob;
+        r.v[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+    } else {
+#pragma unroll
+        for (int q = 0; q < V; ++q) {
+            const int e = tile_elem<D, kVec>(q);
+            const uint32_t off = e < tv ? (uint32_t)((elem_off + e) * D::kBytes) : kOob;
+            uint32_t val;
+            if constexpr (D::kBytes == 4)
+                val = __builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0);
+            else
+                val = __builtin_amdgcn_raw_buffer_load_b16(rsrc, off, 0, 0);
+            r.v[q / 4][q % 4] = val;
+        }
+    }
+}
+
+template <class D, bool kVec>
+__device__ __forceinline__ uint32_t tile_raw(const TileRegs<D, kVec>& r, int q) {
+    if constexpr (kVec && D::kBytes == 2) {
+        const uint32_t w = r.v[0][q >> 1];
+        return (q & 1) ? (w >> 16) : (w & 0xFFFFu);
+    } else {
+        return r.v[q / 4][q % 4];
+    }
+}
+template <class D, bool kVec>
+__device__ __forceinline__ uint32_t tile_word(const TileRegs<D, kVec>& r, int q) {
+    if constexpr (D::kBytes == 4) {
+        return r.v[q / 4][q % 4];
+    } else if constexpr (kVec) {
+        const uint32_t d = r.v[0][q >> 1];
+        return (q & 1) ? d : (d << 16);
+    } else {
+        return r.v[q / 4][q % 4] << 16;
+    }
+}
+
+template <class D, bool kVec>
+__device__ __forceinline__ void generic_tile(Lds<D>& s, RunState& st, const TileRegs<D, kVec>& r, int64_t col0,
+                                             int32_t tv) {
+    constexpr int V = D::kPerLoad;
+    if (tv <= 0) return;
+    uint32_t kmax = 0;
+    if (!st.tset) {
+#pragma unroll
+        for (int q = 0; q < V; ++q) {
+            const int e = tile_elem<D, kVec>(q);
+            if (e < tv) {
+                const uint32_t key = D::key(tile_raw<D, kVec>(r, q));
+                s.keys[st.len + (uint32_t)e] = (typename D::Key)key;
+                s.idx[st.len + (uint32_t)e] = (uint32_t)(col0 + e);
+                kmax = key > kmax ? key : kmax;
+            }
+        }
+        publish_max(s.misc, kmax);
+        st.len += (uint32_t)tv;
+        st.A += (uint32_t)tv;
+        return;
+    }
+    const Thresh th = make_thresh<D>(st.tkey);
+    bool pred[V];
+    uint64_t masks[V];
+#pragma unroll
+    for (int q = 0; q < V; ++q) {
+        pred[q] = tile_elem<D, kVec>(q) < tv && above(tile_word<D, kVec>(r, q), th);
+        masks[q] = __ballot(pred[q]);
+    }
+    const uint32_t added = append_masked<kGW, V>(masks, pred, st.len, s.cnt, st.par, [&](int q, uint32_t pos) {
+        const uint32_t key = D::key(tile_raw<D, kVec>(r, q));
+        s.keys[pos] = (typename D::Key)key;
+        s.idx[pos] = (uint32_t)(col0 + tile_elem<D, kVec>(q));
+        kmax = key > kmax ? key : kmax;
+    });
+    publish_max(s.misc, kmax);
+    st.len += added;
+    st.A += added;
+}
+
+template <class D, bool kVec, int P>
+__device__ void generic_stream(Lds<D>& s, RunState& st, const Params& p, __amdgpu_buffer_rsrc_t rsrc,
+                               int64_t part_elem0, int64_t part_n, int32_t ms) {
+    constexpr int kTE = kGW * 64 * D::kPerLoad;
+    const int64_t B = p.B;
+    const int32_t tpb = (int32_t)ceil_div(B, kTE);
+    const int32_t ntiles = ms * tpb;
+    const uint32_t k = (uint32_t)p.k, B2 = (uint32_t)p.B2;
+    auto tile_geom = [&](int32_t t, int64_t& off, int32_t& tv) {
+        const int32_t bi = t / tpb, sub = t - bi * tpb;
+        if (bi >= ms) {
+            off = 0;
+            tv = 0;
+            return;
+        }
+        const int64_t b = (int64_t)uniform(s.perm[bi]);
+        const int64_t blen = (b * B + B <= part_n) ? B : (part_n - b * B);
+        const int64_t rem = blen - (int64_t)sub * kTE;
+        tv = (int32_t)(rem < kTE ? (rem > 0 ? rem : 0) : kTE);
+        off = b * B + (int64_t)sub * kTE;
+    };
+    TileRegs<D, kVec> ring[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        int64_t off;
+        int32_t tv;
+        tile_geom(j, off, tv);
+        load_tile<D, kVec>(ring[j], rsrc, off, tv);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int32_t t0 = 0; t0 < ntiles; t0 += P) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const int32_t t = t0 + j;
+            if (t < ntiles) {
+                int64_t off;
+                int32_t tv;
+                tile_geom(t, off, tv);
+                generic_tile<D, kVec>(s, st, ring[j], part_elem0 + off, tv);
+                if (t % tpb == tpb - 1) {
+                    st.maxlen = st.len > st.maxlen ? st.len : st.maxlen;
+                    if (st.len >= k + B2) compact<D, kGW>(s, st, k);
+                }
+            }
+            int64_t off;
+            int32_t tv;
+            tile_geom(t + P, off, tv);
+            load_tile<D, kVec>(ring[j], rsrc, off, tv);
+        }
+    }
+}
+
+template <class D, bool kVec>
+__global__ __launch_bounds__(kGW * 64) void deepselect_generic_kernel(Params p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    Lds<D> s = lds_of<D>(smem, p.L);
+    const int64_t items = p.batch * (int64_t)p.split;
+    for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+        const PartGeom g = part_geom(p, item);
+        __syncthreads();
+        clear_hist<kGW>(s.sc.hist);
+        if (threadIdx.x == 0) s.misc[1] = 0u;
+        build_order<kGW>(s.perm, p.seed, g.row, 0, g.b0, g.ms, s.base);
+        RunState st;
+        generic_stream<D, kVec, kVec ? 8 : 4>(s, st, p, part_rsrc<D>(p, g), g.part_elem0, g.part_n, g.ms);
+        final_select<D, kGW>(s, st, (uint32_t)p.k);
+        if (p.split == 1)
+            write_row<D, kGW>(s, p, g.row, st.W, st.A, st.R, st.maxlen);
+        else
+            write_part<D, kGW>(s, st, p, g.slot);
+    }
+}
+
+// ===========================================================================
+// Merge kernel of split rows: DeepSelect over the S part results of a row,
+// one block of k candidates per part, in the random order of tag 1.
+// ===========================================================================
+template <class D>
+__global__ __launch_bounds__(kGW * 64) void deepselect_merge_kernel(Params p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    Lds<D> s = lds_of<D>(smem, p.L);
+    const uint32_t k = (uint32_t)p.k, B2 = (uint32_t)p.B2;
+    const int32_t S = p.split;
+    constexpr uint32_t kTE = kGW * 64 * 4;
+    for (int64_t row = blockIdx.x; row < p.batch; row += gridDim.x) {
+        __syncthreads();
+        clear_hist<kGW>(s.sc.hist);
+        if (threadIdx.x == 0) s.misc[1] = 0u;
+        build_order<kGW>(s.perm, p.seed, row, 1, 0, S, s.base);
+        RunState st;
+        for (int32_t i = 0; i < S; ++i) {
+            const int64_t part = (int64_t)uniform(s.perm[i]);
+            const uint32_t* wk = p.ws_keys + (row * S + part) * (int64_t)k;
+            const uint32_t* wi = p.ws_idx + (row * S + part) * (int64_t)k;
+            for (uint32_t t0 = 0; t0 < k; t0 += kTE) {
+                const uint32_t tv = (k - t0) < kTE ? (k - t0) : kTE;
+                uint32_t kk[4], ii[4];
+                bool inb[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t e = (uint32_t)threadIdx.x * 4u + (uint32_t)q;
+                    inb[q] = e < tv;
+                    kk[q] = inb[q] ? wk[t0 + e] : 0u;
+                    ii[q] = inb[q] ? wi[t0 + e] : 0u;
+                }
+                uint32_t kmax = 0;
+                if (!st.tset) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if (inb[q]) {
+                            const uint32_t pos = st.len + (uint32_t)threadIdx.x * 4u + (uint32_t)q;
+                            s.keys[pos] = (typename D::Key)kk[q];
+                            s.idx[pos] = ii[q];
+                            kmax = kk[q] > kmax ? kk[q] : kmax;
+                        }
+                    }
+                    st.len += tv;
+                    st.A += tv;
+                } else {
+                    bool pred[4];
+                    uint64_t masks[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        pred[q] = inb[q] && kk[q] > st.tkey;
+                        masks[q] = __ballot(pred[q]);
+                    }
+                    const uint32_t added = append_masked<kGW, 4>(masks, pred, st.len, s.cnt, st.par,
+                                                                 [&](int q, uint32_t pos) {
+                                                                     s.keys[pos] = (typename D::Key)kk[q];
+                                                                     s.idx[pos] = ii[q];
+                                                                     kmax = kk[q] > kmax ? kk[q] : kmax;
+                                                                 });
+                    st.len += added;
+                    st.A += added;
+                }
+                publish_max(s.misc, kmax);
+            }
+            st.maxlen = st.len > st.maxlen ? st.len : st.maxlen;
+            if (st.len >= k + B2) compact<D, kGW>(s, st, k);
+        }
+        final_select<D, kGW>(s, st, k);
+        uint64_t W = st.W, A = st.A, R = st.R, maxlen = st.maxlen;
+        for (int32_t q = 0; q < S; ++q) {
+            const uint64_t* o = p.ws_stats + (row * S + q) * DS_STATS_PER_ROW;
+            W += o[DS_STAT_W];
+            A += o[DS_STAT_A];
+            R += o[DS_STAT_R];
+            maxlen = o[DS_STAT_MAX_LEN] > maxlen ? o[DS_STAT_MAX_LEN] : maxlen;
+        }
+        write_row<D, kGW>(s, p, row, W, A, R, maxlen);
+    }
+}
+
+// ===========================================================================
 // Host side.
-// ---------------------------------------------------------------------------
+// ===========================================================================
 
 static int validate_shape(int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int32_t B,
                           int32_t B2) {
@@ -485,9 +744,8 @@ static int validate_shape(int dtype, int64_t batch, int64_t n, int64_t row_strid
 
 static int64_t split_lower_bound(int dtype, int64_t n, int64_t B) {
     const int64_t m = ceil_div(n, B);
-    int64_t lo = ceil_div(m, kPermMax);
-    const int64_t bytes = n * elem_bytes(dtype);
-    lo = std::max<int64_t>(lo, ceil_div(bytes + B * elem_bytes(dtype), kPartBytesMax));
+    const int64_t lo = std::max<int64_t>(ceil_div(m, kPermMax),
+                                         ceil_div((n + B) * elem_bytes(dtype), kPartBytesMax));
     return std::max<int64_t>(lo, 1);
 }
 
@@ -497,24 +755,41 @@ static bool split_ok(int64_t n, int64_t k, int64_t B, int64_t S) {
     return S == 1 || min_part_elems(n, B, S) >= k;
 }
 
-static int lds_check(int dtype, int64_t n, int64_t k, int64_t B, int64_t B2, int64_t S) {
-    if ((int64_t)k + B + B2 > ((int64_t)1 << 30)) return DS_ERR_UNSUPPORTED;
-    const Layout L = make_layout(dtype, n, k, B, B2, S);
-    return L.total <= kLdsLimit ? DS_OK : DS_ERR_UNSUPPORTED;
+// Units (1 KiB per wave) per block on the streaming path; 0 when the block
+// does not fit it (the generic kernel then runs).
+static int stream_units(int dtype, int64_t B) {
+    const int64_t bytes = B * elem_bytes(dtype);
+    if (bytes % 16 != 0) return 0;
+    const int64_t u = ceil_div(bytes, kUnitBytes);
+    if (u <= 1) return 1;
+    if (u <= 2) return 2;
+    if (u <= 4) return 4;
+    if (u <= 8) return 8;
+    return 0;
+}
+
+static bool lds_fits(int dtype, int64_t n, int64_t k, int64_t B, int64_t B2, int64_t S, int waves) {
+    if (k + std::min<int64_t>(B, n) + B2 > ((int64_t)1 << 30)) return false;
+    if (make_layout(dtype, n, k, B, B2, S, waves).total > kLdsLimit) return false;
+    if (S > 1 && make_merge_layout(dtype, k, B2, S, kGW).total > kLdsLimit) return false;
+    return true;
 }
 
 static int plan_split(int dtype, int64_t batch, int64_t n, int32_t k, int32_t B, int32_t B2, int32_t num_cus) {
     const int64_t lo = split_lower_bound(dtype, n, B);
     int64_t S = 1;
-    if (batch > 0 && batch < num_cus) S = ceil_div(num_cus, batch);
+    if (batch > 0 && batch < num_cus / 2) S = ceil_div(num_cus, batch);
     const double bal = std::floor(std::sqrt((double)n * elem_bytes(dtype) / (8.0 * (double)k)));
     S = std::min<int64_t>(S, std::max<int64_t>(1, (int64_t)bal));
     S = std::max<int64_t>(S, lo);
-    while (S > lo && (!split_ok(n, k, B, S) || lds_check(dtype, n, k, B, B2, S) != DS_OK)) --S;
-    if (!split_ok(n, k, B, S)) return DS_ERR_UNSUPPORTED;
-    if (lds_check(dtype, n, k, B, B2, S) != DS_OK) return DS_ERR_UNSUPPORTED;
+    while (S > lo && (!split_ok(n, k, B, S) || !lds_fits(dtype, n, k, B, B2, S, kGW))) --S;
+    if (!split_ok(n, k, B, S) || !lds_fits(dtype, n, k, B, B2, S, kGW)) return DS_ERR_UNSUPPORTED;
     return (int)S;
 }
+
+// Waves per workgroup of the streaming kernel: 8 when the workgroups would
+// leave compute units idle, else 4.
+static int plan_waves(int64_t items, int32_t num_cus) { return items * 2 <= num_cus ? 8 : 4; }
 
 struct DevInfo {
     int cus = 0;
@@ -546,7 +821,7 @@ static int device_info(int dev, DevInfo& out) {
     return DS_OK;
 }
 
-static int library_workspace(int dev, hipStream_t stream, size_t bytes, size_t zero_bytes, void** out) {
+static int library_workspace(int dev, hipStream_t stream, size_t bytes, void** out) {
     std::lock_guard<std::mutex> lk(g_mu);
     WsBuf& w = g_ws[{dev, (void*)stream}];
     if (w.bytes < bytes) {
@@ -558,13 +833,6 @@ static int library_workspace(int dev, hipStream_t stream, size_t bytes, size_t z
         }
         void* ptr = nullptr;
         if (hipMalloc(&ptr, bytes) != hipSuccess) return DS_ERR_HIP;
-        const int64_t words = (int64_t)(zero_bytes / 4);
-        const int grid = (int)std::min<int64_t>(std::max<int64_t>(ceil_div(words, 256), 1), 1024);
-        hipLaunchKernelGGL(zero_u32_kernel, dim3(grid), dim3(256), 0, stream, (uint32_t*)ptr, words);
-        if (hipGetLastError() != hipSuccess) {
-            (void)hipFree(ptr);
-            return DS_ERR_HIP;
-        }
         w.ptr = ptr;
         w.bytes = bytes;
     }
@@ -572,21 +840,47 @@ static int library_workspace(int dev, hipStream_t stream, size_t bytes, size_t z
     return DS_OK;
 }
 
-template <class D, bool kVec, int P>
-static int launch(const Params& prm, size_t lds, hipStream_t stream, int64_t items) {
-    auto kern = deepselect_kernel<D, kVec, P>;
+template <class K>
+static int launch_kernel(K kern, int64_t blocks, int threads, size_t lds, hipStream_t stream, const Params& prm) {
     if (lds > 64 * 1024) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds) != hipSuccess)
             return DS_ERR_HIP;
     }
-    const int64_t grid = std::min<int64_t>(items, (int64_t)1 << 22);
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kWG), lds, stream, prm);
+    const int64_t grid = std::min<int64_t>(blocks, (int64_t)1 << 22);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), lds, stream, prm);
     return hipGetLastError() == hipSuccess ? DS_OK : DS_ERR_HIP;
 }
 
-static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
-                     int32_t B, int32_t B2, uint64_t seed, void* out_vals, int32_t* out_idx, void* stream,
+template <class D, int NW>
+static int launch_stream(int units, const Params& prm, size_t lds, hipStream_t st, int64_t items) {
+    switch (units) {
+        case 1: return launch_kernel(deepselect_stream_kernel<D, NW, 1, 4>, items, NW * 64, lds, st, prm);
+        case 2: return launch_kernel(deepselect_stream_kernel<D, NW, 2, 3>, items, NW * 64, lds, st, prm);
+        case 4: return launch_kernel(deepselect_stream_kernel<D, NW, 4, 2>, items, NW * 64, lds, st, prm);
+        case 8: return launch_kernel(deepselect_stream_kernel<D, NW, 8, 2>, items, NW * 64, lds, st, prm);
+        default: return DS_ERR_UNSUPPORTED;
+    }
+}
+
+template <class D>
+static int launch_all(int units, int waves, bool vec, Params prm, size_t lds, hipStream_t st, int64_t items) {
+    int rc;
+    if (vec && units > 0)
+        rc = waves == 8 ? launch_stream<D, 8>(units, prm, lds, st, items)
+                        : launch_stream<D, 4>(units, prm, lds, st, items);
+    else if (vec)
+        rc = launch_kernel(deepselect_generic_kernel<D, true>, items, kGW * 64, lds, st, prm);
+    else
+        rc = launch_kernel(deepselect_generic_kernel<D, false>, items, kGW * 64, lds, st, prm);
+    if (rc != DS_OK || prm.split == 1) return rc;
+    const int dtype = D::kBytes == 4 ? DS_F32 : DS_BF16;
+    prm.L = make_merge_layout(dtype, prm.k, prm.B2, prm.split, kGW);
+    return launch_kernel(deepselect_merge_kernel<D>, prm.batch, kGW * 64, prm.L.total, st, prm);
+}
+
+static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int32_t B,
+                     int32_t B2, uint64_t seed, void* out_vals, int32_t* out_idx, void* stream,
                      const ds_options_t* opt) {
     int st = validate_shape(dtype, batch, n, row_stride, k, B, B2);
     if (st != DS_OK) return st;
@@ -594,6 +888,8 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     if (!x || !out_vals || !out_idx) return DS_ERR_NULL;
     const int es = elem_bytes(dtype);
     if (((uintptr_t)x % es) != 0) return DS_ERR_SHAPE;
+    const int req_waves = opt ? opt->waves : 0;
+    if (req_waves != 0 && req_waves != 4 && req_waves != 8) return DS_ERR_BLOCK;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DS_ERR_HIP;
     DevInfo di;
@@ -604,11 +900,20 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
         const int ps = plan_split(dtype, batch, n, k, B, B2, di.cus);
         if (ps < 0) return ps;
         S = ps;
-    } else {
-        if (!split_ok(n, k, B, S) || S < split_lower_bound(dtype, n, B)) return DS_ERR_BLOCK;
+    } else if (!split_ok(n, k, B, S) || S < split_lower_bound(dtype, n, B)) {
+        return DS_ERR_BLOCK;
     }
-    if ((st = lds_check(dtype, n, k, B, B2, S)) != DS_OK) return st;
-    const Layout L = make_layout(dtype, n, k, B, B2, S);
+    const bool vec = ((uintptr_t)x % 16 == 0) && ((row_stride * es) % 16 == 0) && (((int64_t)B * es) % 16 == 0) &&
+                     ((n * es) % 16 == 0);
+    const int units = vec ? stream_units(dtype, B) : 0;
+    int waves = units > 0 ? (req_waves ? req_waves : plan_waves(batch * S, di.cus)) : kGW;
+    if (!lds_fits(dtype, n, k, B, B2, S, waves)) {
+        if (waves != kGW && lds_fits(dtype, n, k, B, B2, S, kGW))
+            waves = kGW;
+        else
+            return DS_ERR_UNSUPPORTED;
+    }
+    const Layout L = make_layout(dtype, n, k, B, B2, S, waves);
     if ((int64_t)L.total > (int64_t)di.lds) return DS_ERR_UNSUPPORTED;
 
     Params prm{};
@@ -634,23 +939,17 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
         if (opt && opt->workspace) {
             if (opt->workspace_bytes < wl.total) return DS_ERR_WORKSPACE;
             ws = opt->workspace;
-        } else if ((st = library_workspace(dev, hs, wl.total, wl.keys, &ws)) != DS_OK) {
+        } else if ((st = library_workspace(dev, hs, wl.total, &ws)) != DS_OK) {
             return st;
         }
         unsigned char* w = reinterpret_cast<unsigned char*>(ws);
-        prm.ws_arrive = reinterpret_cast<uint32_t*>(w + wl.arrive);
         prm.ws_keys = reinterpret_cast<uint32_t*>(w + wl.keys);
         prm.ws_idx = reinterpret_cast<uint32_t*>(w + wl.idx);
         prm.ws_stats = reinterpret_cast<uint64_t*>(w + wl.stats);
     }
-    const bool vec = ((uintptr_t)x % 16 == 0) && ((row_stride * es) % 16 == 0) && (((int64_t)B * es) % 16 == 0) &&
-                     ((n * es) % 16 == 0);
-    const int te = kWG * (dtype == DS_F32 ? F32T::kPerLoad : BF16T::kPerLoad);
-    prm.tpb = (int32_t)ceil_div(B, te);
     const int64_t items = batch * S;
-    if (dtype == DS_F32)
-        return vec ? launch<F32T, true, 8>(prm, L.total, hs, items) : launch<F32T, false, 4>(prm, L.total, hs, items);
-    return vec ? launch<BF16T, true, 8>(prm, L.total, hs, items) : launch<BF16T, false, 4>(prm, L.total, hs, items);
+    if (dtype == DS_F32) return launch_all<F32T>(units, waves, vec, prm, L.total, hs, items);
+    return launch_all<BF16T>(units, waves, vec, prm, L.total, hs, items);
 }
 
 }  // namespace ds
@@ -662,12 +961,11 @@ extern "C" {
 
 int deepselect_validate(int dtype, int64_t batch, int64_t N, int64_t row_stride, int32_t k, int32_t B,
                         int32_t B2) {
-    int st = ds::validate_shape(dtype, batch, N, row_stride, k, B, B2);
+    const int st = ds::validate_shape(dtype, batch, N, row_stride, k, B, B2);
     if (st != DS_OK) return st;
-    if (ds::split_lower_bound(dtype, N, B) > 1 &&
-        !ds::split_ok(N, k, B, ds::split_lower_bound(dtype, N, B)))
-        return DS_ERR_UNSUPPORTED;
-    return ds::lds_check(dtype, N, k, B, B2, ds::split_lower_bound(dtype, N, B));
+    const int64_t lo = ds::split_lower_bound(dtype, N, B);
+    if (!ds::split_ok(N, k, B, lo)) return DS_ERR_UNSUPPORTED;
+    return ds::lds_fits(dtype, N, k, B, B2, lo, ds::kGW) ? DS_OK : DS_ERR_UNSUPPORTED;
 }
 
 int deepselect_topk(const void* x, int dtype, int64_t batch, int64_t N, int64_t row_stride, int32_t k, int32_t B,
@@ -705,7 +1003,7 @@ size_t deepselect_workspace_bytes(int dtype, int64_t batch, int64_t N, int32_t k
 
 size_t deepselect_lds_bytes(int dtype, int64_t N, int32_t k, int32_t B, int32_t B2, int32_t split) {
     if (ds::validate_shape(dtype, 1, N, N, k, B, B2) != DS_OK || split < 1) return 0;
-    return ds::make_layout(dtype, N, k, B, B2, split).total;
+    return ds::make_layout(dtype, N, k, B, B2, split, ds::kGW).total;
 }
 
 const char* deepselect_status_string(int status) {
@@ -715,7 +1013,8 @@ const char* deepselect_status_string(int status) {
         case DS_ERR_DTYPE: return "dtype must be DS_F32 or DS_BF16";
         case DS_ERR_SHAPE: return "bad shape: need batch >= 0, 1 <= N < 2^31, row_stride >= N, aligned x";
         case DS_ERR_K: return "k must satisfy 1 <= k <= N";
-        case DS_ERR_BLOCK: return "B and B2 must be >= 1 and a forced split must leave every part >= k elements";
+        case DS_ERR_BLOCK:
+            return "B and B2 must be >= 1; a forced split must leave every part >= k elements; waves 0, 4 or 8";
         case DS_ERR_UNSUPPORTED: return "candidate buffer k+B+B2 (or the block order) does not fit in LDS";
         case DS_ERR_HIP: return "a HIP call failed";
         case DS_ERR_WORKSPACE: return "caller workspace is smaller than deepselect_workspace_bytes";
