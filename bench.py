@@ -24,7 +24,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import math
 import os
@@ -43,16 +42,6 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_digest() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "top_selection_row_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
@@ -63,6 +52,8 @@ def measured_traffic(workload: str):
         d = json.load(open(path))
     except (OSError, ValueError):
         return None
+    from top_selection_row_amd.profiling import source_digest
+
     if d.get("source_digest") != source_digest():
         return None
     return d.get("hbm_bytes_per_launch")
@@ -93,6 +84,28 @@ def cpu_baseline(workload: str, seconds: float):
                       f"rows, {el:.1f} s"}
 
 
+def copy_calibration(args, torch) -> int:
+    """A plain copy of known size: under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE it
+    gives the factor from those counters to bytes actually moved."""
+    n = args.copy_mb * 2**20 // 4
+    src = torch.randint(0, 1 << 30, (n,), dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    print(json.dumps({"mode": "copy", "bytes_read": n * 4, "bytes_written": n * 4, "steps": args.steps,
+                      "ms_per_copy": round(ms, 5), "GBps_read_plus_write": round(2 * n * 4 / ms / 1e6, 1)}),
+          flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +119,10 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-torch", action="store_true", help="skip the torch.topk comparison")
+    ap.add_argument("--mode", choices=("topk", "copy"), default="topk",
+                    help="copy: time a plain device-to-device copy of --copy-mb MiB (the counter "
+                         "calibration run for FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--copy-mb", type=int, default=512)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -116,6 +133,9 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.mode == "copy":
+        return copy_calibration(args, torch)
 
     import synth
     import top_selection_row_amd as ds
