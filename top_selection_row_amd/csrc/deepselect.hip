@@ -74,12 +74,14 @@ template <class D>
 struct Lds {
     typename D::Key* keys;
     uint32_t* idx;
+    uint32_t* hist;
+    uint32_t* fold;
+    uint32_t* tot;
     uint32_t* cnt;
     uint16_t* perm;
-    uint32_t* misc;  // [0] broadcast flag, [1] largest key appended so far
-    SelectScratch sc;
+    uint32_t* misc;  // [1] largest key appended so far
     unsigned char* base;
-    Layout L;
+    uint32_t junk;   // first junk entry of the candidate arrays
 };
 
 template <class D>
@@ -88,62 +90,56 @@ __device__ __forceinline__ Lds<D> lds_of(unsigned char* smem, const Layout& L) {
     s.base = smem;
     s.keys = reinterpret_cast<typename D::Key*>(smem + L.keys);
     s.idx = reinterpret_cast<uint32_t*>(smem + L.idx);
+    s.hist = reinterpret_cast<uint32_t*>(smem + L.hist);
+    s.fold = reinterpret_cast<uint32_t*>(smem + L.fold);
+    s.tot = reinterpret_cast<uint32_t*>(smem + L.tot);
     s.cnt = reinterpret_cast<uint32_t*>(smem + L.cnt);
     s.perm = reinterpret_cast<uint16_t*>(smem + L.perm);
     s.misc = reinterpret_cast<uint32_t*>(smem + L.misc);
-    s.sc.hist = reinterpret_cast<uint32_t*>(smem + L.hist);
-    s.sc.pcnt = reinterpret_cast<uint32_t*>(smem + L.pcnt);
-    s.L = L;
+    s.junk = (uint32_t)L.junk;
     return s;
 }
 
-// Fold this wave's largest appended key into misc[1] (used to skip radix
-// digits that every candidate shares).
+// Start of a (row, part): clear the histogram copies and the largest-key cell
+// (the block order, built next, ends with a barrier).
+template <class D, int NW>
+__device__ __forceinline__ void begin_item(Lds<D>& s) {
+    clear_words<NW>(s.hist, kHistWords);
+    if (threadIdx.x == 0) s.misc[1] = 0u;
+}
+
+// Fold this wave's largest appended key into misc[1] (the top of the key range
+// the radix select starts from).
 __device__ __forceinline__ void publish_max(uint32_t* misc, uint32_t kmax) {
     kmax = wave_max(kmax);
     if (lane_id() == 0 && kmax != 0u) atomicMax(&misc[1], kmax);
 }
 
-// RadixSelectTopK kept out of line so one copy serves every unrolled slot.
-// Arguments and result travel by value so nothing lives in scratch memory, and
-// the LDS arrays are rebuilt here from the workgroup's LDS base and their byte
-// offsets: a pointer passed across the call would lose its address space and
-// turn every access into a flat access.
+// RadixSelectTopK(buffer, k): the buffer keeps its k largest and T becomes the
+// k-th key. Once T is set every candidate is >= T, the bottom of the key range.
 template <class D, int NW>
-__device__ __noinline__ uint32_t compact_call(uint32_t keys_off, uint32_t idx_off, uint32_t hist_off,
-                                              uint32_t pcnt_off, uint32_t misc_off, uint32_t n, uint32_t k,
-                                              uint32_t lo_key) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    SelectScratch sc{reinterpret_cast<uint32_t*>(smem + hist_off), reinterpret_cast<uint32_t*>(smem + pcnt_off)};
-    return radix_select<D, NW>(reinterpret_cast<typename D::Key*>(smem + keys_off),
-                               reinterpret_cast<uint32_t*>(smem + idx_off), n, k, sc, lo_key,
-                               reinterpret_cast<const uint32_t*>(smem + misc_off) + 1);
+__device__ __forceinline__ void select_buffer(Lds<D>& s, RunState& st, uint32_t k) {
+    const uint32_t lo = st.tset ? st.tkey : 0u;
+    __syncthreads();  // appends and the largest key are visible
+    const uint32_t hi = uniform(s.misc[1]);
+    st.tkey = select_topk<D, NW>(s.keys, s.idx, s.hist, s.fold, s.tot, s.junk, st.len, k, lo, hi > lo ? hi : lo);
+    st.tset = true;
+    st.len = k;
 }
 
-template <class D, int NW>
-__device__ __forceinline__ uint32_t select_call(Lds<D>& s, uint32_t n, uint32_t k, uint32_t lo_key) {
-    return compact_call<D, NW>(s.L.keys, s.L.idx, s.L.hist, s.L.pcnt, s.L.misc, n, k, lo_key);
-}
-
-// Compaction: RadixSelectTopK(buffer, k), T = k-th key. Keys are >= T once T
-// is set, which bounds the radix digits from below.
+// Compaction inside the loop (counts in W and R).
 template <class D, int NW>
 __device__ __forceinline__ void compact(Lds<D>& s, RunState& st, uint32_t k) {
     st.W += st.len;
     st.R += 1;
-    st.tkey = select_call<D, NW>(s, st.len, k, st.tset ? st.tkey : 0u);
-    st.tset = true;
-    st.len = k;
+    select_buffer<D, NW>(s, st, k);
 }
 
 // Final RadixSelectTopK (its input length counts in W); ends with a barrier.
 template <class D, int NW>
 __device__ __forceinline__ void final_select(Lds<D>& s, RunState& st, uint32_t k) {
     st.W += st.len;
-    if (st.len > k) {
-        st.tkey = select_call<D, NW>(s, st.len, k, st.tset ? st.tkey : 0u);
-        st.len = k;
-    }
+    if (st.len > k) select_buffer<D, NW>(s, st, k);
     __syncthreads();
 }
 
@@ -177,7 +173,14 @@ __device__ __forceinline__ uint32_t test_word(const BlockRegs<U>& r, int u, int 
     }
 }
 
-template <class D, int NW, int U, int P>
+// A part is streamed in chunks of Q steps; a step hands the next NW blocks of
+// the order to the NW waves. All Q loads of a chunk are issued at its start
+// into Q register slots, so a wave has Q blocks in flight and pays the memory
+// latency about once per chunk. The step loop copies the slot it needs into
+// one working block (a uniform branch per slot, so the copy waits only for
+// that slot's loads), which keeps one copy of the filter, scatter and
+// compaction code and lets the compaction run while later slots still load.
+template <class D, int NW, int U, int Q>
 struct Streamer {
     static constexpr int V = D::kPerLoad;
     static constexpr int UE = 64 * V;  // elements per unit
@@ -223,7 +226,7 @@ struct Streamer {
         }
     }
 
-    // Elements of this wave's block above T (uniform over the wave).
+    // Elements of the block above T (uniform over the wave).
     template <bool kNeg>
     __device__ __forceinline__ uint32_t count_above(const BlockRegs<U>& r, uint32_t thr) const {
         uint32_t c = 0;
@@ -235,7 +238,7 @@ struct Streamer {
         return c;
     }
 
-    // Append every element of this wave's block at base (before the first
+    // Append every element of the block at base (before the first
     // compaction), in element order.
     __device__ __forceinline__ void scatter_all(const BlockRegs<U>& r, uint32_t base, uint32_t boff,
                                                 uint32_t blen) const {
@@ -258,8 +261,8 @@ struct Streamer {
         publish_max(s.misc, kmax);
     }
 
-    // Append the elements of this wave's block above T at base, in (unit,
-    // slot, lane) order.
+    // Append the elements of the block above T at base, in (unit, slot,
+    // lane) order.
     template <bool kNeg>
     __device__ __forceinline__ void scatter_above(const BlockRegs<U>& r, uint32_t base, uint32_t boff,
                                                   uint32_t thr) const {
@@ -286,24 +289,21 @@ struct Streamer {
         publish_max(s.misc, kmax);
     }
 
-    // Count this wave's block against the current state (every element while
-    // the threshold is unset).
-    __device__ __forceinline__ uint32_t count_block(const BlockRegs<U>& r, uint32_t blen) const {
-        if (!st.tset) return blen;
-        const Thresh th = make_thresh<D>(st.tkey);
-        return th.neg ? count_above<true>(r, th.thr) : count_above<false>(r, th.thr);
-    }
-
-    __device__ __forceinline__ void scatter_block(const BlockRegs<U>& r, uint32_t base, uint32_t boff,
-                                                  uint32_t blen) const {
-        if (!st.tset) {
-            scatter_all(r, base, boff, blen);
-        } else {
-            const Thresh th = make_thresh<D>(st.tkey);
-            if (th.neg)
-                scatter_above<true>(r, base, boff, th.thr);
-            else
-                scatter_above<false>(r, base, boff, th.thr);
+    // Copy slot j into the working block: a chain of uniform branches, one per
+    // slot, so the copy of slot q waits only for the loads of slot q. The asm
+    // statement that ends each branch names its slot as an immediate, which
+    // keeps the compiler from merging the branches into one copy from a
+    // variable slot index (that would put the slots in scratch memory).
+    template <int q>
+    __device__ __forceinline__ void take(BlockRegs<U> (&slots)[Q], int32_t j, BlockRegs<U>& r) const {
+        if constexpr (q < Q) {
+            if (j == q) {
+                r = slots[q];
+#pragma unroll
+                for (int u = 0; u < U; ++u) asm volatile("; slot %1" : "+v"(r.v[u]) : "i"(q));
+            } else {
+                take<q + 1>(slots, j, r);
+            }
         }
     }
 
@@ -315,7 +315,16 @@ struct Streamer {
                                                    int32_t first, int32_t nblk) {
         const int w = wave_id();
         const bool mine = w >= first && w < nblk;
-        const uint32_t c = mine ? count_block(r, blen) : 0u;
+        uint32_t c = 0;
+        Thresh th{};
+        if (mine) {
+            if (!st.tset) {
+                c = blen;
+            } else {
+                th = make_thresh<D>(st.tkey);
+                c = th.neg ? count_above<true>(r, th.thr) : count_above<false>(r, th.thr);
+            }
+        }
         if (lane_id() == 0) s.cnt[st.par * NW + w] = c;
         __syncthreads();
         uint32_t cs[NW];
@@ -334,44 +343,50 @@ struct Streamer {
             }
         }
         const int32_t last = trig >= 0 ? trig : nblk - 1;
-        if (mine && w <= last && c != 0) scatter_block(r, my_base, boff, blen);
+        if (mine && w <= last && c != 0) {
+            if (!st.tset)
+                scatter_all(r, my_base, boff, blen);
+            else if (th.neg)
+                scatter_above<true>(r, my_base, boff, th.thr);
+            else
+                scatter_above<false>(r, my_base, boff, th.thr);
+        }
         st.A += run - st.len;
         st.maxlen = run > st.maxlen ? run : st.maxlen;
         st.len = run;
         return trig;
     }
 
-    // One step: the blocks at order positions step*NW + w, w = 0..NW-1. The
-    // common case (no compaction inside the step) is straight-line code; after
-    // a compaction the blocks behind it are counted again against the new T.
-    __device__ __forceinline__ void step(BlockRegs<U>& r, int32_t stp) {
-        uint32_t boff, blen;
-        block_at(stp * NW + wave_id(), boff, blen);
-        if (blen != U * UE) mask_tail(r, blen);
-        const int32_t nblk = ms - stp * NW < NW ? ms - stp * NW : NW;  // blocks in this step
-        int32_t trig = append_from(r, boff, blen, 0, nblk);
-        if (trig >= 0) {
-            compact<D, NW>(s, st, k);
-            while (trig >= 0 && trig < nblk - 1) {
-                trig = append_from(r, boff, blen, trig + 1, nblk);
-                if (trig >= 0) compact<D, NW>(s, st, k);
-            }
-        }
-    }
-
     __device__ __forceinline__ void run() {
         const int w = wave_id();
-        BlockRegs<U> ring[P];
+        for (int32_t c0 = 0; c0 < nsteps; c0 += Q) {
+            BlockRegs<U> slots[Q];
 #pragma unroll
-        for (int j = 0; j < P; ++j) {
-            load(ring[j], j * NW + w);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        for (int32_t s0 = 0; s0 < nsteps; s0 += P) {
-#pragma unroll
-            for (int j = 0; j < P; ++j) {
-                if (s0 + j < nsteps) step(ring[j], s0 + j);
-                load(ring[j], (s0 + j + P) * NW + w);
+            for (int q = 0; q < Q; ++q) load(slots[q], (c0 + q) * NW + w);
+            const int32_t nst = nsteps - c0 < Q ? nsteps - c0 : Q;
+            int32_t j = 0, first = 0;
+            BlockRegs<U> r;
+            uint32_t boff = 0, blen = 0;
+            while (j < nst) {
+                const int32_t stp = c0 + j;
+                const int32_t nblk = ms - stp * NW < NW ? ms - stp * NW : NW;  // blocks in this step
+                if (first == 0) {
+                    block_at(stp * NW + w, boff, blen);
+                    if (w < nblk) {
+                        take<0>(slots, j, r);
+                        if (blen != U * UE) mask_tail(r, blen);
+                    }
+                }
+                const int32_t trig = append_from(r, boff, blen, first, nblk);
+                if (trig >= 0) {
+                    compact<D, NW>(s, st, k);
+                    if (trig < nblk - 1) {
+                        first = trig + 1;  // the blocks behind it, against the new T
+                        continue;
+                    }
+                }
+                ++j;
+                first = 0;
             }
         }
     }
@@ -440,7 +455,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const Params& p, con
                                              (int)(g.part_n * D::kBytes), (int)kRsrcWord3);
 }
 
-template <class D, int NW, int U, int P>
+template <class D, int NW, int U, int Q>
 __global__ __launch_bounds__(NW * 64) void deepselect_stream_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     Lds<D> s = lds_of<D>(smem, p.L);
@@ -448,11 +463,10 @@ __global__ __launch_bounds__(NW * 64) void deepselect_stream_kernel(Params p) {
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const PartGeom g = part_geom(p, item);
         __syncthreads();  // LDS free from the previous item
-        clear_hist<NW>(s.sc.hist);
-        if (threadIdx.x == 0) s.misc[1] = 0u;
+        begin_item<D, NW>(s);
         build_order<NW>(s.perm, p.seed, g.row, 0, g.b0, g.ms, s.base);
         RunState st;
-        Streamer<D, NW, U, P> sm{s,
+        Streamer<D, NW, U, Q> sm{s,
                                  st,
                                  part_rsrc<D>(p, g),
                                  (uint32_t)g.part_elem0,
@@ -477,6 +491,39 @@ __global__ __launch_bounds__(NW * 64) void deepselect_stream_kernel(Params p) {
 // any block size.
 // ===========================================================================
 constexpr int kGW = 4;  // waves of the generic and merge kernels
+
+// Workgroup-cooperative append (one tile spread over all waves): wave counts
+// from the ballot masks, a prefix over the waves through LDS (one barrier),
+// then each survivor's slot from mbcnt. `put(slot, pos)` stores slot's element
+// at buffer position pos. Returns the number appended (uniform).
+template <int NW, int NS, class Put>
+__device__ __forceinline__ uint32_t append_masked(const uint64_t (&masks)[NS], const bool (&pred)[NS],
+                                                  uint32_t len, uint32_t* cnt, uint32_t& par, Put&& put) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int q = 0; q < NS; ++q) c += (uint32_t)__popcll(masks[q]);
+    const int wave = wave_id();
+    if (lane_id() == 0) cnt[par * NW + wave] = c;
+    __syncthreads();
+    uint32_t base = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t cw = cnt[par * NW + w];
+        base += w < wave ? cw : 0u;
+        total += cw;
+    }
+    par ^= 1u;
+    total = uniform(total);
+    if (c != 0) {
+        uint32_t off = len + base;
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+            if (pred[q]) put(q, off + lanes_below(masks[q]));
+            off += (uint32_t)__popcll(masks[q]);
+        }
+    }
+    return total;
+}
 
 template <class D, bool kVec>
 struct TileRegs {
@@ -636,8 +683,7 @@ __global__ __launch_bounds__(kGW * 64) void deepselect_generic_kernel(Params p) 
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const PartGeom g = part_geom(p, item);
         __syncthreads();
-        clear_hist<kGW>(s.sc.hist);
-        if (threadIdx.x == 0) s.misc[1] = 0u;
+        begin_item<D, kGW>(s);
         build_order<kGW>(s.perm, p.seed, g.row, 0, g.b0, g.ms, s.base);
         RunState st;
         generic_stream<D, kVec, kVec ? 8 : 4>(s, st, p, part_rsrc<D>(p, g), g.part_elem0, g.part_n, g.ms);
@@ -662,8 +708,7 @@ __global__ __launch_bounds__(kGW * 64) void deepselect_merge_kernel(Params p) {
     constexpr uint32_t kTE = kGW * 64 * 4;
     for (int64_t row = blockIdx.x; row < p.batch; row += gridDim.x) {
         __syncthreads();
-        clear_hist<kGW>(s.sc.hist);
-        if (threadIdx.x == 0) s.misc[1] = 0u;
+        begin_item<D, kGW>(s);
         build_order<kGW>(s.perm, p.seed, row, 1, 0, S, s.base);
         RunState st;
         for (int32_t i = 0; i < S; ++i) {
@@ -852,12 +897,14 @@ static int launch_kernel(K kern, int64_t blocks, int threads, size_t lds, hipStr
     return hipGetLastError() == hipSuccess ? DS_OK : DS_ERR_HIP;
 }
 
+// Register slots per wave: Q blocks of U 16-byte loads in flight, 32 loads
+// (128 VGPRs) at most.
 template <class D, int NW>
 static int launch_stream(int units, const Params& prm, size_t lds, hipStream_t st, int64_t items) {
     switch (units) {
-        case 1: return launch_kernel(deepselect_stream_kernel<D, NW, 1, 4>, items, NW * 64, lds, st, prm);
-        case 2: return launch_kernel(deepselect_stream_kernel<D, NW, 2, 3>, items, NW * 64, lds, st, prm);
-        case 4: return launch_kernel(deepselect_stream_kernel<D, NW, 4, 2>, items, NW * 64, lds, st, prm);
+        case 1: return launch_kernel(deepselect_stream_kernel<D, NW, 1, 16>, items, NW * 64, lds, st, prm);
+        case 2: return launch_kernel(deepselect_stream_kernel<D, NW, 2, 8>, items, NW * 64, lds, st, prm);
+        case 4: return launch_kernel(deepselect_stream_kernel<D, NW, 4, 4>, items, NW * 64, lds, st, prm);
         case 8: return launch_kernel(deepselect_stream_kernel<D, NW, 8, 2>, items, NW * 64, lds, st, prm);
         default: return DS_ERR_UNSUPPORTED;
     }

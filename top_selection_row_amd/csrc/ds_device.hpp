@@ -4,11 +4,11 @@
 //   ("CUDA 算子笔记 4", milkfeng.top, section "改造 Radix Sort", float_to_key);
 // * the random block order (SplitMix64 of Steele, Lea and Flood, OOPSLA 2014,
 //   used as a counter-based hash; ids sorted by (hash, id));
-// * RadixSelectTopK in LDS: MSD select over 8-bit digits with per-wave private
+// * RadixSelectTopK in LDS: MSD select over 8-bit digits with privatised
 //   histograms ("改造 Radix Sort"; "并行算法（一）", elainafan.one, section
 //   "Histogram" on privatisation), then an in-place stable partition keeping
 //   the k largest (the predicate -> scan -> scatter "Compact" of
-//   "并行算法（一）", done with 64-bit ballot masks and mbcnt ranks).
+//   "并行算法（一）", with DPP prefix sums inside a wave).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -172,41 +172,6 @@ __device__ void build_order(uint16_t* perm, uint64_t seed, int64_t row, int tag,
     __syncthreads();
 }
 
-// ----------------------------------------------------------------------------
-// Workgroup-cooperative append (one tile spread over all waves): wave counts
-// from the ballot masks, a prefix over the NW waves through LDS (one barrier),
-// then each survivor's slot from mbcnt. `put(slot, pos)` stores slot's element
-// at buffer position pos. Returns the number appended (uniform).
-// ----------------------------------------------------------------------------
-template <int NW, int NS, class Put>
-__device__ __forceinline__ uint32_t append_masked(const uint64_t (&masks)[NS], const bool (&pred)[NS],
-                                                  uint32_t len, uint32_t* cnt, uint32_t& par, Put&& put) {
-    uint32_t c = 0;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) c += (uint32_t)__popcll(masks[s]);
-    const int wave = wave_id();
-    if (lane_id() == 0) cnt[par * NW + wave] = c;
-    __syncthreads();
-    uint32_t base = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const uint32_t cw = cnt[par * NW + w];
-        base += w < wave ? cw : 0u;
-        total += cw;
-    }
-    par ^= 1u;
-    total = uniform(total);
-    if (c != 0) {
-        uint32_t off = len + base;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            if (pred[s]) put(s, off + lanes_below(masks[s]));
-            off += (uint32_t)__popcll(masks[s]);
-        }
-    }
-    return total;
-}
-
 // Largest value over the wave, returned uniform (a DPP max scan whose last
 // lane holds the maximum; lanes outside a move contribute 0).
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
@@ -243,217 +208,273 @@ __device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v) {
 // ----------------------------------------------------------------------------
 // RadixSelectTopK in LDS.
 //
-// Histograms: one shared set of kHistCopies copies of the 256 bins, bin-major
-// (word b*16 + c is copy c of bin b); lane l adds into copy l % 16. Lanes that
-// share a bin therefore hit at most 4 words, and the 16 copies of a bin sit in
-// 16 different LDS banks, so an atomic wave instruction costs at most a few
-// conflict cycles even when every key falls into one bin (LDS atomics
-// serialise per word). After the atomics the workgroup folds the copies into
-// a compact 256-bin array, clearing them on the way.
+// The candidates are read in chunks of 8 consecutive entries: chunk c covers
+// entries [8c, 8c+8) and round r of a workgroup of NT threads gives chunk
+// r*NT + t to thread t. Keys are read 16 bytes at a time.
+//
+// Digits are relative to the range the keys are known to lie in: a pass over
+// keys in [base, base+span] uses digit (key - base) >> s, s the smallest shift
+// that leaves at most 256 digits, so a pass resolves 8 bits of the span rather
+// than 8 fixed bits of the key (once T is set the span is the distance from T
+// to the largest key appended, often under 256).
+//
+// Histograms: 16 copies of 256 16-bit counters, two bins per word; lane l adds
+// into copy l % 16, word (d / 2) * 16 + l % 16. The 16 copies of a word sit in
+// 16 different banks, so lanes that share a digit hit at most 4 words of it.
+// A fold sums the copies into 256 bins and clears them.
 // ----------------------------------------------------------------------------
-constexpr int kHistCopies = 16;
-constexpr int kHistWords = 256 * kHistCopies;  // plus 256 words of folded bins after them
+constexpr uint32_t kHistCopies = 16;
+constexpr uint32_t kHistWords = 128 * kHistCopies;  // 8 KiB
 
-struct SelectScratch {
-    uint32_t* hist;  // kHistWords copies, then 256 folded bins
-    uint32_t* pcnt;  // 2 x NW x 2
+template <class D>
+struct KeyChunk {
+    u32x4 v[D::kBytes == 4 ? 2 : 1];
 };
 
-// Clear every histogram copy (each thread its share; caller adds the barrier).
-template <int NW>
-__device__ __forceinline__ void clear_hist(uint32_t* hist) {
-    u32x4* h = reinterpret_cast<u32x4*>(hist);
-    for (int i = threadIdx.x; i < kHistWords / 4; i += NW * 64) h[i] = u32x4{0u, 0u, 0u, 0u};
+template <class D>
+__device__ __forceinline__ void read_chunk(KeyChunk<D>& kc, const typename D::Key* keys, uint32_t c) {
+    const u32x4* kv = reinterpret_cast<const u32x4*>(keys) + c * (D::kBytes == 4 ? 2u : 1u);
+    kc.v[0] = kv[0];
+    if constexpr (D::kBytes == 4) kc.v[1] = kv[1];
 }
 
-// Fold the copies into folded[256] and clear them (caller adds the barriers).
+template <class D>
+__device__ __forceinline__ uint32_t chunk_key(const KeyChunk<D>& kc, int i) {
+    if constexpr (D::kBytes == 4)
+        return kc.v[i >> 2][i & 3];
+    else
+        return (kc.v[0][i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+}
+
+// Clear `words` words of LDS (each thread its share; caller adds the barrier).
 template <int NW>
-__device__ __forceinline__ void fold_hist(uint32_t* hist) {
-    constexpr int kPer = kHistWords / (NW * 64);  // words per thread (multiple of 4)
-    static_assert(kHistWords % (NW * 64 * 4) == 0, "fold split");
-    constexpr int kThreadsPerBin = kHistCopies / kPer;
-    u32x4* h = reinterpret_cast<u32x4*>(hist) + threadIdx.x * (kPer / 4);
-    uint32_t sum = 0;
+__device__ __forceinline__ void clear_words(uint32_t* p, uint32_t words) {
+    u32x4* h = reinterpret_cast<u32x4*>(p);
+    for (uint32_t i = threadIdx.x; i < words / 4; i += NW * 64) h[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// Add every key of keys[0, n) with key - base <= span into the digit
+// (key - base) >> s of this lane's histogram copy. A key slot that no lane of
+// the wave counts is skipped (a uniform branch); otherwise every lane adds,
+// the ones that do not count add zero.
+template <class D, int NW>
+__device__ __forceinline__ void hist_pass(const typename D::Key* keys, uint32_t n, uint32_t base, uint32_t span,
+                                          int s, uint32_t* hist) {
+    constexpr uint32_t NT = NW * 64;
+    const uint32_t nch = (n + kChunk - 1) / kChunk;
+    uint32_t* hl = hist + (lane_id() & (kHistCopies - 1));
+    for (uint32_t c0 = 0; c0 < nch; c0 += NT) {
+        const uint32_t c = c0 + threadIdx.x;
+        KeyChunk<D> kc;
+        read_chunk<D>(kc, keys, c < nch ? c : 0u);
+        const uint32_t lim = c < nch ? n - c * kChunk : 0u;  // valid entries of this chunk
 #pragma unroll
-    for (int j = 0; j < kPer / 4; ++j) {
+        for (int i = 0; i < kChunk; ++i) {
+            const uint32_t u = chunk_key<D>(kc, i) - base;
+            const bool ok = (uint32_t)i < lim && u <= span;
+            if (__ballot(ok) != 0ull) {
+                const uint32_t d = (u >> s) & 255u;
+                atomicAdd(&hl[(d >> 1) * kHistCopies], ok ? 1u << ((d & 1u) * 16) : 0u);
+            }
+        }
+    }
+}
+
+// Fold the copies into folded[256] and clear them (caller adds barriers).
+// Thread t sums the words [4t, 4t+4) (or [8t, 8t+8) with 4 waves): copies of
+// bins 2g and 2g+1, g = word / 16; the threads of a group combine with DPP
+// shifts and the last of them writes the two bins.
+template <int NW>
+__device__ __forceinline__ void fold_pass(uint32_t* hist, uint32_t* folded) {
+    constexpr int NT = NW * 64;
+    constexpr int WPT = kHistWords / NT;      // words per thread (4 or 8)
+    constexpr int TPG = kHistCopies / WPT;    // threads per group (4 or 2)
+    static_assert(WPT % 4 == 0 && TPG >= 1, "fold split");
+    const int t = threadIdx.x, g = t / TPG;
+    u32x4* h = reinterpret_cast<u32x4*>(hist) + t * (WPT / 4);
+    uint32_t a = 0, b = 0;
+#pragma unroll
+    for (int j = 0; j < WPT / 4; ++j) {
         const u32x4 v = h[j];
-        sum += v.x + v.y + v.z + v.w;
+        a += (v.x & 0xFFFFu) + (v.y & 0xFFFFu) + (v.z & 0xFFFFu) + (v.w & 0xFFFFu);
+        b += (v.x >> 16) + (v.y >> 16) + (v.z >> 16) + (v.w >> 16);
         h[j] = u32x4{0u, 0u, 0u, 0u};
     }
-    if constexpr (kThreadsPerBin == 2) sum += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sum, 0x111, 0xF, 0xF, true);
-    if constexpr (kThreadsPerBin == 4) {
-        sum += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sum, 0x111, 0xF, 0xF, true);
-        sum += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sum, 0x112, 0xF, 0xF, true);
+    if constexpr (TPG >= 2) {
+        a += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x111, 0xF, 0xF, true);
+        b += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b, 0x111, 0xF, 0xF, true);
     }
-    if ((threadIdx.x % kThreadsPerBin) == kThreadsPerBin - 1) hist[kHistWords + threadIdx.x / kThreadsPerBin] = sum;
+    if constexpr (TPG >= 4) {
+        a += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x112, 0xF, 0xF, true);
+        b += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b, 0x112, 0xF, 0xF, true);
+    }
+    if (t % TPG == TPG - 1) reinterpret_cast<uint2*>(folded)[g] = uint2{a, b};
+}
+
+// The bin of folded[256] that holds the rank-th largest key (every wave, same
+// answer): lane l takes bins 4*(63-l) .. 4*(63-l)+3, a prefix sum over lanes
+// counts the keys from the top bin down, the first lane reaching rank names
+// the group and a 4-bin step the bin. rank becomes the rank inside that bin.
+__device__ __forceinline__ uint32_t pick_bin(const uint32_t* folded, uint32_t& rank) {
+    const int lane = lane_id();
+    const u32x4 c = reinterpret_cast<const u32x4*>(folded)[63 - lane];
+    const uint32_t s = c.x + c.y + c.z + c.w;
+    const uint32_t incl = wave_prefix_sum(s);
+    const uint64_t ge = __ballot(incl >= rank);
+    const int L = __builtin_ctzll(ge);
+    const int g = 63 - L;
+    uint32_t above_cnt = uniform(__builtin_amdgcn_readlane(incl - s, L));
+    const uint32_t c3 = uniform(__builtin_amdgcn_readlane(c.w, L));
+    const uint32_t c2 = uniform(__builtin_amdgcn_readlane(c.z, L));
+    const uint32_t c1 = uniform(__builtin_amdgcn_readlane(c.y, L));
+    uint32_t d;
+    if (above_cnt + c3 >= rank) {
+        d = 4u * g + 3u;
+    } else if (above_cnt + c3 + c2 >= rank) {
+        above_cnt += c3;
+        d = 4u * g + 2u;
+    } else if (above_cnt + c3 + c2 + c1 >= rank) {
+        above_cnt += c3 + c2;
+        d = 4u * g + 1u;
+    } else {
+        above_cnt += c3 + c2 + c1;
+        d = 4u * g;
+    }
+    rank -= above_cnt;
+    return d;
 }
 
 // Stable in-place partition of keys/idx[0, n): keep every key > kth and the
-// first `need` keys == kth in buffer order, packed into [0, k). Rounds of
-// 64*NW*R entries: each wave reads its 64*R entries into registers and
-// publishes (greater, tied) counts; after one barrier every destination is
-// known and lies at or before its source, so no round overwrites an entry
-// that is still to be read.
-template <class KeyT, int NW, int R = 8>
-__device__ void partition_keep(KeyT* keys, uint32_t* idx, uint32_t n, uint32_t kth, uint32_t need,
-                               uint32_t* pcnt) {
-    const int lane = lane_id(), wave = wave_id();
-    uint32_t sel_run = 0, tie_run = 0, par = 0;
-    for (uint32_t base = 0; base < n; base += NW * 64 * R) {
-        const uint32_t wbase = base + (uint32_t)wave * 64u * R;
-        uint32_t kk[R], ii[R];
-        uint64_t gm[R], tm[R];
-        uint32_t g = 0, t = 0;
+// first `need` keys == kth, in buffer order, packed into [0, k). Groups of up
+// to kRoundsPerGroup rounds: every thread counts the greater and tied entries
+// of its chunks (low and high 16 bits of one word), a DPP prefix sum inside
+// the wave and one LDS exchange of the wave totals (one barrier per group)
+// give each chunk the number of kept entries before it, and a second walk
+// over the chunk stores the kept entries there. A destination never passes
+// the entry's own position, so no group overwrites an entry a later group
+// still reads. Dropped entries are stored to a per-lane junk slot past the
+// buffer, so the stores need no branch.
+template <class D, int NW>
+__device__ __forceinline__ void partition_keep(typename D::Key* keys, uint32_t* idx, uint32_t* tot, uint32_t n,
+                                               uint32_t kth, uint32_t need, uint32_t junk) {
+    constexpr int NT = NW * 64, R = kRoundsPerGroup;
+    const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const uint32_t nch = (n + kChunk - 1) / kChunk;
+    const uint32_t my_junk = junk + (uint32_t)lane;
+    uint32_t run = 0, par = 0;  // greater | tied << 16 before this group
+    for (uint32_t c0 = 0; c0 < nch; c0 += NT * R) {
+        const int nr = nch - c0 > (uint32_t)NT ? R : 1;  // rounds of this group holding chunks
+        KeyChunk<D> kc[R];
+        u32x4 ix[R][2];
+        uint32_t lim[R], mine[R], incl[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const uint32_t pos = wbase + (uint32_t)r * 64u + (uint32_t)lane;
-            const bool v = pos < n;
-            kk[r] = v ? (uint32_t)keys[pos] : 0u;
-            ii[r] = v ? idx[pos] : 0u;
-        }
+            if (r < nr) {
+                const uint32_t c = c0 + r * NT + t;
+                const bool has = c < nch;
+                const uint32_t cr = has ? c : 0u;
+                read_chunk<D>(kc[r], keys, cr);
+                const u32x4* iv = reinterpret_cast<const u32x4*>(idx) + cr * 2u;
+                ix[r][0] = iv[0];
+                ix[r][1] = iv[1];
+                lim[r] = has ? n - c * kChunk : 0u;
+                uint32_t g = 0, e = 0;
+                if (__ballot(lim[r] < (uint32_t)kChunk) == 0ull) {  // every chunk of the wave is full
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint32_t pos = wbase + (uint32_t)r * 64u + (uint32_t)lane;
-            const bool v = pos < n;
-            gm[r] = __ballot(v & (kk[r] > kth));
-            tm[r] = __ballot(v & (kk[r] == kth));
-            g += (uint32_t)__popcll(gm[r]);
-            t += (uint32_t)__popcll(tm[r]);
-        }
-        if (lane == 0) {
-            pcnt[(par * NW + wave) * 2 + 0] = g;
-            pcnt[(par * NW + wave) * 2 + 1] = t;
+                    for (int i = 0; i < kChunk; ++i) {
+                        const uint32_t key = chunk_key<D>(kc[r], i);
+                        g += key > kth ? 1u : 0u;
+                        e += key == kth ? 1u : 0u;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < kChunk; ++i) {
+                        const uint32_t key = chunk_key<D>(kc[r], i);
+                        const bool v = (uint32_t)i < lim[r];
+                        g += (v && key > kth) ? 1u : 0u;
+                        e += (v && key == kth) ? 1u : 0u;
+                    }
+                }
+                mine[r] = g | (e << 16);
+                incl[r] = wave_prefix_sum(mine[r]);
+                if (lane == 63) tot[(par * R + r) * NW + wave] = incl[r];
+            }
         }
         __syncthreads();
-        uint32_t sel_before = sel_run, tie_before = tie_run, sel_round = 0, tie_round = 0;
+        const u32x4* tv = reinterpret_cast<const u32x4*>(tot + par * R * NW);
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const uint32_t gw = uniform(pcnt[(par * NW + w) * 2 + 0]);
-            const uint32_t tw = uniform(pcnt[(par * NW + w) * 2 + 1]);
-            const uint32_t prior = tie_run + tie_round;
-            const uint32_t room = need > prior ? need - prior : 0u;
-            const uint32_t sw = gw + (tw < room ? tw : room);
-            if (w < wave) {
-                sel_before += sw;
-                tie_before += tw;
+        for (int r = 0; r < R; ++r) {
+            if (r < nr) {
+                uint32_t before = run, all = 0;  // packed counts before this wave / in this round
+#pragma unroll
+                for (int w4 = 0; w4 < NW / 4; ++w4) {
+                    const u32x4 x = tv[(r * NW) / 4 + w4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        before += (w4 * 4 + q < wave) ? x[q] : 0u;
+                        all += x[q];
+                    }
+                }
+                const uint32_t excl = before + incl[r] - mine[r];
+                uint32_t tie = excl >> 16;
+                uint32_t dst = (excl & 0xFFFFu) + (tie < need ? tie : need);
+                if (__ballot(lim[r] < (uint32_t)kChunk) == 0ull) {
+#pragma unroll
+                    for (int i = 0; i < kChunk; ++i) {
+                        const uint32_t key = chunk_key<D>(kc[r], i);
+                        const bool eq = key == kth;
+                        const bool kp = key > kth || (eq && tie < need);
+                        const uint32_t at = kp ? dst : my_junk;
+                        keys[at] = (typename D::Key)key;
+                        idx[at] = ix[r][i >> 2][i & 3];
+                        dst += kp ? 1u : 0u;
+                        tie += eq ? 1u : 0u;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < kChunk; ++i) {
+                        const uint32_t key = chunk_key<D>(kc[r], i);
+                        const bool v = (uint32_t)i < lim[r];
+                        const bool eq = v && key == kth;
+                        const bool kp = (v && key > kth) || (eq && tie < need);
+                        const uint32_t at = kp ? dst : my_junk;
+                        keys[at] = (typename D::Key)key;
+                        idx[at] = ix[r][i >> 2][i & 3];
+                        dst += kp ? 1u : 0u;
+                        tie += eq ? 1u : 0u;
+                    }
+                }
+                run += all;
             }
-            sel_round += sw;
-            tie_round += tw;
         }
         par ^= 1u;
-        uint32_t sb = sel_before, tb = tie_before;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint32_t pos = wbase + (uint32_t)r * 64u + (uint32_t)lane;
-            const bool v = pos < n;
-            const bool is_gt = v & (kk[r] > kth);
-            const bool is_tie = v & (kk[r] == kth);
-            const bool sel = is_gt | (is_tie & (tb + lanes_below(tm[r]) < need));
-            const uint64_t sm = __ballot(sel);
-            if (sel) {
-                const uint32_t dst = sb + lanes_below(sm);
-                keys[dst] = (KeyT)kk[r];
-                idx[dst] = ii[r];
-            }
-            tb += (uint32_t)__popcll(tm[r]);
-            sb += (uint32_t)__popcll(sm);
-        }
-        sel_run += sel_round;
-        tie_run += tie_round;
     }
 }
 
-// Histogram of the digit (key >> shift) & 255 of every key of keys[0, n) that
-// matches `prefix` under `pmask`. Keys are read 16 bytes at a time (4 or 8
-// keys per lane) so the LDS reads pipeline; lane l adds into copy l % 16.
-template <class KeyT, int NW>
-__device__ __forceinline__ void histogram_pass(const KeyT* keys, uint32_t n, uint32_t prefix, uint32_t pmask,
-                                               int shift, uint32_t* hist) {
-    constexpr int kPer = 16 / sizeof(KeyT);
-    uint32_t* hc = hist + (lane_id() & (kHistCopies - 1));
-    const uint32_t nvec = n / kPer;
-    const u32x4* kv = reinterpret_cast<const u32x4*>(keys);
-    for (uint32_t i = threadIdx.x; i < nvec; i += NW * 64) {
-        const u32x4 v = kv[i];
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-            uint32_t key;
-            if constexpr (sizeof(KeyT) == 4)
-                key = v[q];
-            else
-                key = (v[q >> 1] >> ((q & 1) * 16)) & 0xFFFFu;
-            if ((key & pmask) == prefix) atomicAdd(&hc[((key >> shift) & 0xFFu) * kHistCopies], 1u);
-        }
-    }
-    for (uint32_t i = nvec * kPer + threadIdx.x; i < n; i += NW * 64) {
-        const uint32_t key = keys[i];
-        if ((key & pmask) == prefix) atomicAdd(&hc[((key >> shift) & 0xFFu) * kHistCopies], 1u);
-    }
-}
-
-// Keep the k largest of keys/idx[0, n) (n > k) in [0, k); return the k-th key.
-// MSD select over 8-bit digits: each pass histograms the digit of every key
-// that matches the prefix fixed so far, folds the copies, and every wave walks
-// the folded bins from the top to the one holding the rank-th largest (a
-// 64-lane DPP prefix scan over the bins in descending order plus a 4-bin
-// step). Passes start at the highest bit where the smallest and largest
-// possible key (lo_key, *hi_ptr) differ: higher bits are shared by all keys.
-// The histogram copies must be clear on entry; they are clear on return.
+// RadixSelectTopK: keep the k largest of keys/idx[0, n) (k <= n) in [0, k)
+// and return the k-th largest key. Every key lies in [lo, hi]. Entries
+// [junk, junk+64) of both arrays are scratch for dropped entries. Starts with a
+// barrier (the caller's appends become visible); the histogram copies must be
+// clear on entry and are clear on return.
 template <class D, int NW>
-__device__ uint32_t radix_select(typename D::Key* keys, uint32_t* idx, uint32_t n, uint32_t k, SelectScratch& sc,
-                                 uint32_t lo_key, const uint32_t* hi_ptr) {
-    const int lane = lane_id();
-    __syncthreads();  // every append / earlier partition is visible
-    const uint32_t hi_key = uniform(*hi_ptr);
-    const uint32_t diff = lo_key ^ (hi_key > lo_key ? hi_key : lo_key);
-    const int top = diff ? 31 - __clz(diff) : 0;  // highest differing bit
-    // first window [top-7, top] (clamped at 0); shared bits above it are fixed
-    int shift = top >= 7 ? top - 7 : 0;
-    uint32_t pmask = (shift + 8 >= 32) ? 0u : ~((1u << (shift + 8)) - 1u);
-    uint32_t prefix = lo_key & pmask, rank = k;
-    const uint32_t* folded = sc.hist + kHistWords;
+__device__ uint32_t select_topk(typename D::Key* keys, uint32_t* idx, uint32_t* hist, uint32_t* folded,
+                                uint32_t* tot, uint32_t junk, uint32_t n, uint32_t k, uint32_t lo, uint32_t hi) {
+    __syncthreads();
+    uint32_t base = lo, span = hi - lo, rank = k;
+    int s = span ? 32 - __clz(span) : 0;  // bit length of the span
+    s = s > 8 ? s - 8 : 0;
     while (true) {
-        histogram_pass<typename D::Key, NW>(keys, n, prefix, pmask, shift, sc.hist);
+        hist_pass<D, NW>(keys, n, base, span, s, hist);
         __syncthreads();
-        fold_hist<NW>(sc.hist);
+        fold_pass<NW>(hist, folded);
         __syncthreads();
-        // lane l holds bins 4*(63-l) .. 4*(63-l)+3, so a prefix sum over lanes
-        // counts the keys in the bins from the top down to this lane's lowest
-        const u32x4 c = reinterpret_cast<const u32x4*>(folded)[63 - lane];
-        const uint32_t s = c.x + c.y + c.z + c.w;
-        const uint32_t incl = wave_prefix_sum(s);
-        const uint64_t ge = __ballot(incl >= rank);
-        const int L = __builtin_ctzll(ge);  // first lane (from the top bins) reaching rank
-        const int g = 63 - L;               // its bin group
-        uint32_t above_cnt = uniform(__builtin_amdgcn_readlane(incl - s, L));
-        const uint32_t c3 = uniform(__builtin_amdgcn_readlane(c.w, L));
-        const uint32_t c2 = uniform(__builtin_amdgcn_readlane(c.z, L));
-        const uint32_t c1 = uniform(__builtin_amdgcn_readlane(c.y, L));
-        uint32_t d;
-        if (above_cnt + c3 >= rank) {
-            d = 4u * g + 3u;
-        } else if (above_cnt + c3 + c2 >= rank) {
-            above_cnt += c3;
-            d = 4u * g + 2u;
-        } else if (above_cnt + c3 + c2 + c1 >= rank) {
-            above_cnt += c3 + c2;
-            d = 4u * g + 1u;
-        } else {
-            above_cnt += c3 + c2 + c1;
-            d = 4u * g;
-        }
-        rank -= above_cnt;
-        prefix |= d << shift;
-        pmask |= 0xFFu << shift;
-        if (shift == 0) break;
-        // next window; when it reaches below bit 8 it is [0, 7] and may overlap
-        // bits already fixed -- every matching key agrees on those bits, so the
-        // histogram and the prefix stay consistent
-        shift = shift >= 8 ? shift - 8 : 0;
-        __syncthreads();  // every wave has read the folded bins
+        base += pick_bin(folded, rank) << s;
+        if (s == 0) break;
+        span = (1u << s) - 1u;
+        s = s > 8 ? s - 8 : 0;
     }
-    partition_keep<typename D::Key, NW>(keys, idx, n, prefix, rank, sc.pcnt);
-    return prefix;
+    partition_keep<D, NW>(keys, idx, tot, n, base, rank, junk);
+    return base;
 }
 
 }  // namespace ds

@@ -24,6 +24,8 @@ constexpr int64_t kPermMax = 8192;        // blocks per part kept in the LDS blo
 constexpr int64_t kMaxSplit = 1024;       // parts per row
 constexpr size_t kLdsLimit = 160 * 1024;  // gfx950 LDS per workgroup
 constexpr int64_t kPartBytesMax = (int64_t)1 << 31;  // 32-bit buffer offsets per part
+constexpr int kChunk = 8;                 // candidate entries per thread and select round
+constexpr int kRoundsPerGroup = 2;        // select rounds whose entries a thread holds at once
 
 DS_HD inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 DS_HD inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -50,15 +52,18 @@ inline int64_t min_part_elems(int64_t n, int64_t B, int64_t S) {
 
 // Dynamic LDS layout of one workgroup (byte offsets from the start of LDS).
 struct Layout {
-    uint32_t keys;   // cap candidate keys (uint32 for f32, uint16 for bf16)
-    uint32_t idx;    // cap candidate column indices (uint32)
-    uint32_t hist;   // 16 interleaved copies of 256 bins, then 256 folded bins (uint32)
+    uint32_t keys;   // cap candidate keys (uint32 for f32, uint16 for bf16), padded to 8 entries,
+                     // then 64 junk entries (stores of dropped entries)
+    uint32_t idx;    // cap candidate column indices (uint32), the same padding and junk
+    uint32_t hist;   // radix histogram: 16 copies of 256 16-bit counters (8 KiB)
+    uint32_t fold;   // 256 folded bins (uint32)
+    uint32_t tot;    // 2 x rounds x waves per-wave totals of the select partition
     uint32_t cnt;    // 2 x waves per-wave counts (block loop)
-    uint32_t pcnt;   // 2 x waves x 2 per-wave counts (partition)
     uint32_t perm;   // block order (uint16 per block)
     uint32_t misc;   // 16 uint32 of broadcast scratch
     uint32_t total;  // bytes
     int32_t cap;     // candidate buffer capacity in entries
+    int32_t junk;    // first junk entry (cap padded to 8)
     int32_t waves;   // waves per workgroup the layout was made for
 };
 
@@ -69,26 +74,31 @@ inline int64_t capacity(int64_t k, int64_t blk, int64_t B2) { return k + blk + B
 // order_n: ids in the random order (blocks of the largest part, or parts).
 inline Layout make_layout_raw(int key_bytes, int64_t cap, int64_t order_n, int waves) {
     Layout L{};
+    const int64_t capp = ceil_div(cap, kChunk) * kChunk;
+    const int64_t entries = capp + 64;
     size_t off = 0;
     L.keys = 0;
-    off = align_up((size_t)cap * key_bytes, 16);
+    off = align_up((size_t)entries * key_bytes, 16);
     L.idx = (uint32_t)off;
-    off = align_up(off + (size_t)cap * 4, 16);
+    off = align_up(off + (size_t)entries * 4, 16);
     // Building the block order uses the candidate arrays as scratch before the
     // scan starts: an 8-byte hash and a 4-byte rank or id per entry.
     off = std::max(off, align_up((size_t)next_pow2(std::max<int64_t>(order_n, 1)) * 12, 16));
     L.hist = (uint32_t)off;
-    off += (size_t)(256 * 16 + 256) * 4;
+    off += (size_t)16 * 128 * 4;
+    L.fold = (uint32_t)off;
+    off += 256 * 4;
+    L.tot = (uint32_t)off;
+    off += align_up((size_t)2 * kRoundsPerGroup * waves * 4, 16);
     L.cnt = (uint32_t)off;
     off += align_up((size_t)2 * waves * 4, 16);
-    L.pcnt = (uint32_t)off;
-    off += align_up((size_t)2 * waves * 2 * 4, 16);
     L.perm = (uint32_t)off;
     off = align_up(off + (size_t)order_n * 2, 16);
     L.misc = (uint32_t)off;
     off += 16 * 4;
     L.total = (uint32_t)align_up(off, 16);
     L.cap = (int32_t)cap;
+    L.junk = (int32_t)capp;
     L.waves = waves;
     return L;
 }
