@@ -114,6 +114,8 @@ def main() -> int:
     ap.add_argument("--workload", default="dsa128k_bf16")
     ap.add_argument("--split", type=int, default=0, help="parts per row (0 = library choice)")
     ap.add_argument("--waves", type=int, default=0, help="waves per workgroup (0 = library choice)")
+    ap.add_argument("--kernel", type=int, default=0,
+                    help="0 library choice, 1 ring streaming, 2 register streaming, 3 generic")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--rotate-mb", type=int, default=768)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -169,7 +171,7 @@ def main() -> int:
         log(f"[bench] no valid split: {ds.deepselect_status_string(split)}")
         return 1
     lib = ds.library()
-    opt = ds.DsOptions(int(split), int(args.waves), None, None, 0)
+    opt = ds.DsOptions(int(split), int(args.waves), None, None, 0, int(args.kernel))
     ptrs = [rot[i].data_ptr() for i in range(copies)]
     vptr, iptr = vals.data_ptr(), idx.data_ptr()
     fn = lib.deepselect_topk_ex

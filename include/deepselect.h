@@ -90,6 +90,13 @@ typedef struct ds_options {
      * kernel, so it must not be shared by calls that may overlap. */
     void *workspace;
     size_t workspace_bytes;
+    /* Kernel: 0 = library choice; 1 = ring streaming (blocks copied HBM -> LDS
+     * into a per-wave ring; DS_ERR_UNSUPPORTED when the ring does not fit in
+     * LDS); 2 = register streaming (blocks held in registers); 3 = generic
+     * (the workgroup shares each block; any layout). 1 and 2 apply to rows the
+     * streaming kernels take (see `waves`); others run the generic kernel.
+     * Any other value: DS_ERR_BLOCK. */
+    int32_t kernel;
 } ds_options_t;
 
 /* Check arguments only (pure host code, no HIP call; usable without a GPU).

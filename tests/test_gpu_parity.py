@@ -50,9 +50,9 @@ def raw_of(t):
     raise TypeError(t.dtype)
 
 
-def run_gpu(x: np.ndarray, k, B, B2, seed=0, split=0, stats=True, waves=0):
+def run_gpu(x: np.ndarray, k, B, B2, seed=0, split=0, stats=True, waves=0, kernel=0):
     xt = to_device(x)
-    out = ds.topk(xt, k, B, B2, seed, split=split, stats=stats, waves=waves)
+    out = ds.topk(xt, k, B, B2, seed, split=split, stats=stats, waves=waves, kernel=kernel)
     torch.cuda.synchronize()
     vals, idx = raw_of(out[0]), out[1].cpu().numpy()
     st = out[2].cpu().numpy() if stats else None
@@ -131,6 +131,25 @@ def test_forced_waves(name, split, waves):
     vals, idx, st = run_gpu(x, w.k, w.block, w.block2, seed=5, split=split, waves=waves)
     check_rows(x, vals, idx, w.k)
     check_stats_against_model(x, st, w.k, w.block, w.block2, 5, split, range(min(rows, 4)))
+
+
+KERNELS = {1: "ring", 2: "registers", 3: "generic"}
+
+
+@pytest.mark.parametrize("name,split,waves,kernel", [
+    (name, split, waves, kernel)
+    for kernel in (1, 2, 3)
+    for name, split, waves in [("dsa128k_bf16", 1, 8), ("dsa128k_bf16", 2, 4), ("dsa32k", 4, 8),
+                               ("vocab152k_k1024", 1, 4), ("asc1m", 8, 8), ("ties1m", 8, 4),
+                               ("gauss4k", 1, 8)]])
+def test_each_kernel(name, split, waves, kernel):
+    w = synth.WORKLOADS[name]
+    rows = min(w.batch, 12)
+    log(f"[gpu] kernel {KERNELS[kernel]} {name} S={split} waves={waves} rows {rows}")
+    x = synth.generate(name, rows)
+    vals, idx, st = run_gpu(x, w.k, w.block, w.block2, seed=7, split=split, waves=waves, kernel=kernel)
+    check_rows(x, vals, idx, w.k)
+    check_stats_against_model(x, st, w.k, w.block, w.block2, 7, split, range(min(rows, 4)))
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2, 2**63 + 5])

@@ -34,7 +34,7 @@ EXPORTS = (
 class DsOptions(ctypes.Structure):
     _fields_ = [("split", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("stats", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("kernel", ctypes.c_int32)]
 
 
 _lib = None
@@ -120,8 +120,8 @@ def deepselect_topk(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals, ou
 
 
 def deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals, out_idx, stream,
-                       split=0, stats=None, workspace=None, workspace_bytes=0, waves=0) -> int:
-    opt = DsOptions(int(split), int(waves), stats, workspace, int(workspace_bytes))
+                       split=0, stats=None, workspace=None, workspace_bytes=0, waves=0, kernel=0) -> int:
+    opt = DsOptions(int(split), int(waves), stats, workspace, int(workspace_bytes), int(kernel))
     return library().deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed & (2**64 - 1),
                                         out_vals, out_idx, stream, ctypes.byref(opt))
 
@@ -129,8 +129,11 @@ def deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals,
 # ---------------------------------------------------------------- torch wrapper
 
 def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, waves: int = 0,
-         stats: bool = False, out=None, stream=None):
+         kernel: int = 0, stats: bool = False, out=None, stream=None):
     """Row-wise top-k of a 2-D CUDA tensor (float32 or bfloat16, unit column stride).
+
+    ``kernel``: 0 library choice, 1 ring streaming, 2 register streaming,
+    3 generic (``ds_options_t.kernel`` of the C header).
 
     Returns (vals [batch, k] same dtype, idx [batch, k] int32) and, with
     ``stats=True``, a [batch, 4] int64 tensor (W, A, R, max_len). The k entries
@@ -161,7 +164,7 @@ def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, waves: in
     with torch.cuda.device(x.device):
         _check(deepselect_topk_ex(x.data_ptr(), dt, batch, n, row_stride, k, B, B2, seed,
                                   vals.data_ptr(), idx.data_ptr(), stream, split=split, waves=waves,
-                                  stats=st.data_ptr() if st is not None else None))
+                                  kernel=kernel, stats=st.data_ptr() if st is not None else None))
     if stats:
         return vals, idx, st
     return vals, idx

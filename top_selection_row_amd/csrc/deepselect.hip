@@ -392,6 +392,245 @@ struct Streamer {
     }
 };
 
+// ---------------------------------------------------------------------------
+// Ring streaming: blocks travel HBM -> LDS with buffer loads that write LDS
+// directly (no registers held while they fly), into a ring of `depth` block
+// slots per wave. A step waits (vmcnt) only for its own block, reads it into
+// registers, and refills the slot with the block `depth` steps ahead.
+// ---------------------------------------------------------------------------
+// s_waitcnt that waits until at most N vector-memory operations are
+// outstanding and leaves the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// s_waitcnt for every outstanding LDS operation of the wave.
+__device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+template <class D, int NW, int U>
+struct RingStreamer {
+    static constexpr int V = D::kPerLoad;
+    static constexpr int UE = 64 * V;  // elements per unit
+
+    Lds<D>& s;
+    RunState& st;
+    const __amdgpu_buffer_rsrc_t rsrc;
+    const uint32_t part_elem0, part_n, B;  // parts hold < 2^31 bytes
+    const int32_t ms, nsteps, depth;
+    const uint32_t k, B2;
+    u32x4* ring;  // this wave's slots: slot q unit u at ring[(q*U + u)*64 + lane]
+
+    __device__ __forceinline__ void block_at(int32_t bi, uint32_t& boff, uint32_t& blen) const {
+        if (bi >= ms) {
+            boff = 0;
+            blen = 0;
+            return;
+        }
+        boff = uniform(s.perm[bi]) * B;
+        const uint32_t rem = part_n - boff;
+        blen = rem < B ? rem : B;
+    }
+
+    // Start copying the block at order position bi into slot q (U buffer
+    // loads of 16 bytes per lane; lanes past the block read nothing).
+    __device__ __forceinline__ void fetch(int32_t bi, int32_t q) const {
+        uint32_t boff, blen;
+        block_at(bi, boff, blen);
+        const uint32_t lane = lane_id();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t e0 = u * UE + lane * V;
+            const uint32_t off = e0 + V <= blen ? (boff + e0) * D::kBytes : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void*)(ring + (q * U + u) * 64), 16, off, 0, 0, 0);
+        }
+    }
+
+    // Wait until the block with `ahead` blocks fetched after it has landed.
+    __device__ __forceinline__ void wait_block(int32_t ahead) const {
+        if (ahead <= 0)
+            wait_vm<0>();
+        else if (ahead == 1)
+            wait_vm<U>();
+        else if (ahead == 2)
+            wait_vm<2 * U>();
+        else
+            wait_vm<3 * U>();
+    }
+
+    __device__ __forceinline__ void read_slot(int32_t q, BlockRegs<U>& r) const {
+        const uint32_t lane = lane_id();
+#pragma unroll
+        for (int u = 0; u < U; ++u) r.v[u] = ring[(q * U + u) * 64 + lane];
+    }
+
+    // Lanes past the end of a short block hold zeros; give them all-ones bits
+    // instead, whose key is 0: never above any threshold.
+    __device__ __forceinline__ void mask_tail(BlockRegs<U>& r, uint32_t blen) const {
+        const uint32_t lane = lane_id();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u * UE + lane * V >= blen) r.v[u] = u32x4{~0u, ~0u, ~0u, ~0u};
+        }
+    }
+
+    // This lane's elements above T: one 32-bit compare per element (the
+    // threshold's sign is fixed at compile time), summed per lane.
+    template <bool kNeg>
+    __device__ __forceinline__ uint32_t lane_above(const BlockRegs<U>& r, uint32_t thr) const {
+        uint32_t c = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int q = 0; q < V; ++q) c += above_k<kNeg>(test_word<D, U>(r, u, q), thr) ? 1u : 0u;
+        }
+        return c;
+    }
+
+    // This lane's elements inside the block (every element is admitted before
+    // the first compaction).
+    __device__ __forceinline__ uint32_t lane_valid(uint32_t blen) const {
+        const uint32_t lane = lane_id();
+        uint32_t c = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t e0 = u * UE + lane * V;
+            c += e0 >= blen ? 0u : (blen - e0 < (uint32_t)V ? blen - e0 : (uint32_t)V);
+        }
+        return c;
+    }
+
+    // Append this lane's admitted elements at pos, in element order (lanes in
+    // order, so the wave's survivors fill [base, base + count) lane by lane).
+    // A slot that admits nothing in the whole wave is skipped; otherwise the
+    // lanes that do not admit it store to their junk entry.
+    template <int kMode>  // 0: every element inside the block; 1: above T (T >= 0); 2: above T (T < 0)
+    __device__ __forceinline__ void scatter(const BlockRegs<U>& r, uint32_t pos, uint32_t boff, uint32_t blen,
+                                            uint32_t thr) const {
+        // laundered like the block in append_from: per-slot columns and
+        // bounds must not be hoisted out of the retry loop either
+        uint32_t lane = lane_id();
+        asm volatile("" : "+v"(lane));
+        const uint32_t col0 = part_elem0 + boff + lane * V;
+        const uint32_t junk = s.junk + lane;
+        uint32_t kmax = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int q = 0; q < V; ++q) {
+                bool pred;
+                if constexpr (kMode == 0)
+                    pred = u * UE + lane * V + q < blen;
+                else
+                    pred = above_k<kMode == 2>(test_word<D, U>(r, u, q), thr);
+                if (__ballot(pred) != 0ull) {
+                    const uint32_t key = D::key(raw_at<D, U>(r, u, q));
+                    const uint32_t at = pred ? pos : junk;
+                    s.keys[at] = (typename D::Key)key;
+                    s.idx[at] = col0 + (uint32_t)(u * UE + q);
+                    pos += pred ? 1u : 0u;
+                    kmax = pred && key > kmax ? key : kmax;
+                }
+                // one slot at a time: keeps the compiler from computing every
+                // slot's key and column up front (register pressure)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        publish_max(s.misc, kmax);
+    }
+
+    // Blocks first..nblk-1 of the step counted against the current state, then
+    // appended in order up to (and including) the first block after which the
+    // buffer holds k + B2 or more. Returns that block's wave, or -1.
+    __device__ __forceinline__ int32_t append_from(const BlockRegs<U>& r0, uint32_t boff, uint32_t blen,
+                                                   int32_t first, int32_t nblk) {
+        // The block passes through an empty asm statement here, so nothing
+        // derived from it (keys, shifted words, columns of every slot) can be
+        // hoisted out of the step's retry loop and held in registers.
+        BlockRegs<U> r = r0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) asm volatile("" : "+v"(r.v[u]));
+        const int w = wave_id();
+        const bool mine = w >= first && w < nblk;
+        uint32_t lc = 0;
+        Thresh th{};
+        if (mine) {
+            if (!st.tset) {
+                lc = lane_valid(blen);
+            } else {
+                th = make_thresh<D>(st.tkey);
+                lc = th.neg ? lane_above<true>(r, th.thr) : lane_above<false>(r, th.thr);
+            }
+        }
+        const uint32_t incl = wave_prefix_sum(lc);
+        const uint32_t c = uniform(__builtin_amdgcn_readlane(incl, 63));
+        if (lane_id() == 0) s.cnt[st.par * NW + w] = c;
+        __syncthreads();
+        uint32_t cs[NW];
+#pragma unroll
+        for (int g = 0; g < NW; ++g) cs[g] = uniform(s.cnt[st.par * NW + g]);
+        st.par ^= 1u;
+        // the pages' order: block after block, compaction check after each
+        uint32_t run = st.len, my_base = 0;
+        int32_t trig = -1;
+#pragma unroll
+        for (int g = 0; g < NW; ++g) {
+            if (g >= first && g < nblk && trig < 0) {
+                if (g == w) my_base = run;
+                run += cs[g];
+                if (run >= k + B2) trig = g;
+            }
+        }
+        const int32_t last = trig >= 0 ? trig : nblk - 1;
+        if (mine && w <= last && c != 0) {
+            const uint32_t pos = my_base + incl - lc;
+            if (!st.tset)
+                scatter<0>(r, pos, boff, blen, 0u);
+            else if (th.neg)
+                scatter<2>(r, pos, boff, blen, th.thr);
+            else
+                scatter<1>(r, pos, boff, blen, th.thr);
+        }
+        st.A += run - st.len;
+        st.maxlen = run > st.maxlen ? run : st.maxlen;
+        st.len = run;
+        return trig;
+    }
+
+    __device__ __forceinline__ void run() {
+        const int w = wave_id();
+        int32_t issued = 0;  // steps whose block of this wave is fetched
+        for (; issued < depth && issued < nsteps; ++issued) fetch(issued * NW + w, issued);
+        BlockRegs<U> r;
+        for (int32_t stp = 0; stp < nsteps; ++stp) {
+            const int32_t q = stp % depth;
+            const int32_t nblk = ms - stp * NW < NW ? ms - stp * NW : NW;  // blocks in this step
+            uint32_t boff, blen;
+            block_at(stp * NW + w, boff, blen);
+            wait_block(issued - 1 - stp);
+            read_slot(q, r);
+            if (w < nblk && blen != U * UE) mask_tail(r, blen);
+            int32_t first = 0;
+            while (true) {
+                const int32_t trig = append_from(r, boff, blen, first, nblk);
+                if (trig < 0) break;
+                compact<D, NW>(s, st, k);
+                if (trig >= nblk - 1) break;
+                first = trig + 1;  // the blocks behind it, against the new T
+            }
+            if (issued < nsteps) {
+                wait_lgkm();  // this wave's reads of slot q are done before it is refilled
+                fetch(issued * NW + w, q);
+                ++issued;
+            }
+        }
+    }
+};
+
+template <class D, int NW, int U>
+__global__ __launch_bounds__(NW * 64) void deepselect_ring_kernel(Params p);
+
 template <class D, int NW>
 __device__ __forceinline__ void write_row(Lds<D>& s, const Params& p, int64_t row, uint64_t W, uint64_t A,
                                           uint64_t R, uint64_t maxlen) {
@@ -476,6 +715,39 @@ __global__ __launch_bounds__(NW * 64) void deepselect_stream_kernel(Params p) {
                                  (int32_t)ceil_div(g.ms, NW),
                                  (uint32_t)p.k,
                                  (uint32_t)p.B2};
+        sm.run();
+        final_select<D, NW>(s, st, (uint32_t)p.k);
+        if (p.split == 1)
+            write_row<D, NW>(s, p, g.row, st.W, st.A, st.R, st.maxlen);
+        else
+            write_part<D, NW>(s, st, p, g.slot);
+    }
+}
+
+template <class D, int NW, int U>
+__global__ __launch_bounds__(NW * 64) void deepselect_ring_kernel(Params p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    Lds<D> s = lds_of<D>(smem, p.L);
+    u32x4* ring = reinterpret_cast<u32x4*>(smem + p.L.ring) + (size_t)wave_id() * p.L.ring_depth * U * 64;
+    const int64_t items = p.batch * (int64_t)p.split;
+    for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+        const PartGeom g = part_geom(p, item);
+        __syncthreads();  // LDS free from the previous item
+        begin_item<D, NW>(s);
+        build_order<NW>(s.perm, p.seed, g.row, 0, g.b0, g.ms, s.base);
+        RunState st;
+        RingStreamer<D, NW, U> sm{s,
+                                  st,
+                                  part_rsrc<D>(p, g),
+                                  (uint32_t)g.part_elem0,
+                                  (uint32_t)g.part_n,
+                                  (uint32_t)p.B,
+                                  g.ms,
+                                  (int32_t)ceil_div(g.ms, NW),
+                                  p.L.ring_depth,
+                                  (uint32_t)p.k,
+                                  (uint32_t)p.B2,
+                                  ring};
         sm.run();
         final_select<D, NW>(s, st, (uint32_t)p.k);
         if (p.split == 1)
@@ -910,10 +1182,28 @@ static int launch_stream(int units, const Params& prm, size_t lds, hipStream_t s
     }
 }
 
+template <class D, int NW>
+static int launch_ring(int units, const Params& prm, size_t lds, hipStream_t st, int64_t items) {
+    switch (units) {
+        case 1: return launch_kernel(deepselect_ring_kernel<D, NW, 1>, items, NW * 64, lds, st, prm);
+        case 2: return launch_kernel(deepselect_ring_kernel<D, NW, 2>, items, NW * 64, lds, st, prm);
+        case 4: return launch_kernel(deepselect_ring_kernel<D, NW, 4>, items, NW * 64, lds, st, prm);
+        case 8: return launch_kernel(deepselect_ring_kernel<D, NW, 8>, items, NW * 64, lds, st, prm);
+        default: return DS_ERR_UNSUPPORTED;
+    }
+}
+
+// Kernel choice: ring streaming when the ring fits, else register streaming;
+// the generic kernel for rows the streaming kernels do not take.
+enum KernelKind { kAuto = 0, kRing = 1, kRegs = 2, kGeneric = 3 };
+
 template <class D>
-static int launch_all(int units, int waves, bool vec, Params prm, size_t lds, hipStream_t st, int64_t items) {
+static int launch_all(KernelKind kind, int units, int waves, bool vec, Params prm, hipStream_t st, int64_t items) {
     int rc;
-    if (vec && units > 0)
+    const size_t lds = prm.L.total;
+    if (kind == kRing)
+        rc = waves == 8 ? launch_ring<D, 8>(units, prm, lds, st, items) : launch_ring<D, 4>(units, prm, lds, st, items);
+    else if (kind == kRegs)
         rc = waves == 8 ? launch_stream<D, 8>(units, prm, lds, st, items)
                         : launch_stream<D, 4>(units, prm, lds, st, items);
     else if (vec)
@@ -953,15 +1243,29 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     const bool vec = ((uintptr_t)x % 16 == 0) && ((row_stride * es) % 16 == 0) && (((int64_t)B * es) % 16 == 0) &&
                      ((n * es) % 16 == 0);
     const int units = vec ? stream_units(dtype, B) : 0;
-    int waves = units > 0 ? (req_waves ? req_waves : plan_waves(batch * S, di.cus)) : kGW;
+    const int req_kernel = opt ? opt->kernel : 0;
+    if (req_kernel < kAuto || req_kernel > kGeneric) return DS_ERR_BLOCK;
+    KernelKind kind = units > 0 ? kAuto : kGeneric;
+    if (req_kernel == kGeneric) kind = kGeneric;
+    int waves = kind != kGeneric ? (req_waves ? req_waves : plan_waves(batch * S, di.cus)) : kGW;
     if (!lds_fits(dtype, n, k, B, B2, S, waves)) {
         if (waves != kGW && lds_fits(dtype, n, k, B, B2, S, kGW))
             waves = kGW;
         else
             return DS_ERR_UNSUPPORTED;
     }
-    const Layout L = make_layout(dtype, n, k, B, B2, S, waves);
+    Layout L = make_layout(dtype, n, k, B, B2, S, waves);
     if ((int64_t)L.total > (int64_t)di.lds) return DS_ERR_UNSUPPORTED;
+    if (kind != kGeneric) {
+        const Layout LR = with_ring(L, ceil_div(ceil_div(ceil_div(n, B), S), waves), units, (size_t)di.lds);
+        if (req_kernel == kRing && LR.ring_depth == 0) return DS_ERR_UNSUPPORTED;
+        if (req_kernel == kRegs || LR.ring_depth == 0) {
+            kind = kRegs;
+        } else {
+            kind = kRing;
+            L = LR;
+        }
+    }
 
     Params prm{};
     prm.x = x;
@@ -995,8 +1299,8 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
         prm.ws_stats = reinterpret_cast<uint64_t*>(w + wl.stats);
     }
     const int64_t items = batch * S;
-    if (dtype == DS_F32) return launch_all<F32T>(units, waves, vec, prm, L.total, hs, items);
-    return launch_all<BF16T>(units, waves, vec, prm, L.total, hs, items);
+    if (dtype == DS_F32) return launch_all<F32T>(kind, units, waves, vec, prm, hs, items);
+    return launch_all<BF16T>(kind, units, waves, vec, prm, hs, items);
 }
 
 }  // namespace ds

@@ -61,9 +61,12 @@ struct Layout {
     uint32_t cnt;    // 2 x waves per-wave counts (block loop)
     uint32_t perm;   // block order (uint16 per block)
     uint32_t misc;   // 16 uint32 of broadcast scratch
+    uint32_t ring;   // streaming ring: waves x ring_depth blocks of ring_units KiB (0 if none)
     uint32_t total;  // bytes
     int32_t cap;     // candidate buffer capacity in entries
     int32_t junk;    // first junk entry (cap padded to 8)
+    int32_t ring_depth;  // blocks per wave in the ring (0: no ring)
+    int32_t ring_units;  // KiB per block slot
     int32_t waves;   // waves per workgroup the layout was made for
 };
 
@@ -107,6 +110,23 @@ inline Layout make_layout_raw(int key_bytes, int64_t cap, int64_t order_n, int w
 inline Layout make_layout(int dtype, int64_t n, int64_t k, int64_t B, int64_t B2, int64_t S, int waves) {
     const int64_t m = ceil_div(n, B);
     return make_layout_raw(elem_bytes(dtype), capacity(k, std::min<int64_t>(B, n), B2), ceil_div(m, S), waves);
+}
+
+// Add a streaming ring to a layout: every wave gets `depth` slots of `units`
+// KiB, depth as large as LDS allows up to kRingMax (and no more than the steps
+// of a part). Leaves the layout without a ring when fewer than 2 slots fit.
+constexpr int kRingMax = 4;
+inline Layout with_ring(Layout L, int64_t steps, int units, size_t lds_limit) {
+    const size_t base = align_up(L.total, 16);
+    const size_t per = (size_t)L.waves * units * kUnitBytes;
+    int64_t depth = base < lds_limit ? (int64_t)((lds_limit - base) / per) : 0;
+    depth = std::min<int64_t>({depth, (int64_t)kRingMax, std::max<int64_t>(steps, 1)});
+    if (depth < 2 && !(depth == 1 && steps <= 1)) return L;
+    L.ring = (uint32_t)base;
+    L.ring_depth = (int32_t)depth;
+    L.ring_units = units;
+    L.total = (uint32_t)(base + per * depth);
+    return L;
 }
 
 // Layout of the merge kernel of split rows: S blocks of k candidates.
