@@ -77,9 +77,11 @@ struct Lds {
     uint32_t* hist;
     uint32_t* fold;
     uint32_t* tot;
+    uint32_t* gathered;
+    uint32_t* sparse;   // 64 words per wave (ring streaming: few-survivor scatter)
     uint32_t* cnt;
     uint16_t* perm;
-    uint32_t* misc;  // [1] largest key appended so far
+    uint32_t* misc;  // [1] largest key appended so far, [2] gathered-key counter
     unsigned char* base;
     uint32_t junk;   // first junk entry of the candidate arrays
 };
@@ -93,6 +95,8 @@ __device__ __forceinline__ Lds<D> lds_of(unsigned char* smem, const Layout& L) {
     s.hist = reinterpret_cast<uint32_t*>(smem + L.hist);
     s.fold = reinterpret_cast<uint32_t*>(smem + L.fold);
     s.tot = reinterpret_cast<uint32_t*>(smem + L.tot);
+    s.gathered = reinterpret_cast<uint32_t*>(smem + L.gather);
+    s.sparse = reinterpret_cast<uint32_t*>(smem + L.sparse);
     s.cnt = reinterpret_cast<uint32_t*>(smem + L.cnt);
     s.perm = reinterpret_cast<uint16_t*>(smem + L.perm);
     s.misc = reinterpret_cast<uint32_t*>(smem + L.misc);
@@ -122,7 +126,8 @@ __device__ __forceinline__ void select_buffer(Lds<D>& s, RunState& st, uint32_t 
     const uint32_t lo = st.tset ? st.tkey : 0u;
     __syncthreads();  // appends and the largest key are visible
     const uint32_t hi = uniform(s.misc[1]);
-    st.tkey = select_topk<D, NW>(s.keys, s.idx, s.hist, s.fold, s.tot, s.junk, st.len, k, lo, hi > lo ? hi : lo);
+    st.tkey = select_topk<D, NW>(s.keys, s.idx, s.hist, s.fold, s.tot, s.gathered, s.misc + 2, s.junk, st.len, k, lo,
+                                  hi > lo ? hi : lo);
     st.tset = true;
     st.len = k;
 }
@@ -475,17 +480,32 @@ struct RingStreamer {
         }
     }
 
-    // This lane's elements above T: one 32-bit compare per element (the
-    // threshold's sign is fixed at compile time), summed per lane.
+    // This lane's elements above T as a bit mask (element u*V + q of the lane
+    // at bit u*V + q; blocks of more than 32 elements per lane keep only the
+    // count, in the low bits, with bit 31 set), one 32-bit compare per element
+    // (the threshold's sign fixed at compile time).
+    static constexpr bool kMasks = U * V <= 32;
     template <bool kNeg>
-    __device__ __forceinline__ uint32_t lane_above(const BlockRegs<U>& r, uint32_t thr) const {
-        uint32_t c = 0;
+    __device__ __forceinline__ uint32_t lane_mask(const BlockRegs<U>& r, uint32_t thr) const {
+        uint32_t m = 0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
-            for (int q = 0; q < V; ++q) c += above_k<kNeg>(test_word<D, U>(r, u, q), thr) ? 1u : 0u;
+            for (int q = 0; q < V; ++q) {
+                const bool p = above_k<kNeg>(test_word<D, U>(r, u, q), thr);
+                if constexpr (kMasks)
+                    m |= p ? 1u << (u * V + q) : 0u;
+                else
+                    m += p ? 1u : 0u;
+            }
         }
-        return c;
+        return m;
+    }
+    __device__ __forceinline__ static uint32_t mask_count(uint32_t m) {
+        if constexpr (kMasks)
+            return (uint32_t)__builtin_popcount(m);
+        else
+            return m;
     }
 
     // This lane's elements inside the block (every element is admitted before
@@ -505,11 +525,56 @@ struct RingStreamer {
     // order, so the wave's survivors fill [base, base + count) lane by lane).
     // A slot that admits nothing in the whole wave is skipped; otherwise the
     // lanes that do not admit it store to their junk entry.
-    template <int kMode>  // 0: every element inside the block; 1: above T (T >= 0); 2: above T (T < 0)
-    __device__ __forceinline__ void scatter(const BlockRegs<U>& r, uint32_t pos, uint32_t boff, uint32_t blen,
-                                            uint32_t thr) const {
-        // laundered like the block in append_from: per-slot columns and
-        // bounds must not be hoisted out of the retry loop either
+    // Key of every element of a 32-bit word (bfloat16: both halves).
+    __device__ __forceinline__ static uint32_t word_keys(uint32_t d) {
+        if constexpr (D::kBytes == 4) {
+            return key_f32(d);
+        } else {
+            const uint32_t neg = ((d >> 15) & 0x00010001u) * 0xFFFFu;
+            return d ^ (neg | 0x80008000u);
+        }
+    }
+    __device__ __forceinline__ static uint32_t word_max(uint32_t kw) {
+        if constexpr (D::kBytes == 4) {
+            return kw;
+        } else {
+            const uint32_t lo = kw & 0xFFFFu, hi = kw >> 16;
+            return lo > hi ? lo : hi;
+        }
+    }
+
+    // Append every element inside the block (before the first compaction).
+    __device__ __forceinline__ void scatter_valid(const BlockRegs<U>& r, uint32_t pos, uint32_t boff,
+                                                  uint32_t blen) const {
+        uint32_t lane = lane_id();
+        asm volatile("" : "+v"(lane));  // nothing here may be hoisted out of the retry loop
+        const uint32_t col0 = part_elem0 + boff + lane * V;
+        const uint32_t junk = s.junk + lane;
+        uint32_t kmax = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int q = 0; q < V; ++q) {
+                const bool pred = u * UE + lane * V + q < blen;
+                const uint32_t key = D::key(raw_at<D, U>(r, u, q));
+                const uint32_t at = pred ? pos : junk;
+                s.keys[at] = (typename D::Key)key;
+                s.idx[at] = col0 + (uint32_t)(u * UE + q);
+                pos += pred ? 1u : 0u;
+                kmax = pred && key > kmax ? key : kmax;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        publish_max(s.misc, kmax);
+    }
+
+    // Append the lane's elements above T (mask m) at pos in element order.
+    // A slot no lane of the wave admits is skipped; otherwise the lanes that
+    // do not admit it store to their junk entry. The largest key appended is
+    // the block's largest key, since that one is admitted whenever any is.
+    template <class MaskT>
+    __device__ __forceinline__ void scatter_dense(const BlockRegs<U>& r, MaskT m, uint32_t pos,
+                                                  uint32_t boff) const {
         uint32_t lane = lane_id();
         asm volatile("" : "+v"(lane));
         const uint32_t col0 = part_elem0 + boff + lane * V;
@@ -518,24 +583,103 @@ struct RingStreamer {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
-            for (int q = 0; q < V; ++q) {
-                bool pred;
-                if constexpr (kMode == 0)
-                    pred = u * UE + lane * V + q < blen;
-                else
-                    pred = above_k<kMode == 2>(test_word<D, U>(r, u, q), thr);
-                if (__ballot(pred) != 0ull) {
-                    const uint32_t key = D::key(raw_at<D, U>(r, u, q));
-                    const uint32_t at = pred ? pos : junk;
-                    s.keys[at] = (typename D::Key)key;
-                    s.idx[at] = col0 + (uint32_t)(u * UE + q);
-                    pos += pred ? 1u : 0u;
-                    kmax = pred && key > kmax ? key : kmax;
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t kw = word_keys(r.v[u][w]);
+                const uint32_t wm = word_max(kw);
+                kmax = wm > kmax ? wm : kmax;
+#pragma unroll
+                for (int h = 0; h < V / 4; ++h) {
+                    const int q = w * (V / 4) + h;
+                    const bool pred = (m >> (u * V + q)) & 1;
+                    if (__ballot(pred) != 0ull) {
+                        const uint32_t at = pred ? pos : junk;
+                        s.keys[at] = (typename D::Key)(h ? kw >> 16 : kw);
+                        s.idx[at] = col0 + (uint32_t)(u * UE + q);
+                        pos += pred ? 1u : 0u;
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                // one slot at a time: keeps the compiler from computing every
-                // slot's key and column up front (register pressure)
-                __builtin_amdgcn_sched_barrier(0);
             }
+        }
+        publish_max(s.misc, kmax);
+    }
+
+    // Few survivors in the wave (c <= 64): survivor j is written by lane j.
+    // Every lane lists its survivors in the wave's scratch (lane id and rank
+    // inside the lane, at its exclusive prefix excl), then lane j takes entry
+    // j, fetches that lane's mask with a lane permute, finds the element of
+    // that rank and reads it back from the block's ring slot.
+    __device__ __forceinline__ void scatter_sparse(uint32_t m, uint32_t excl, uint32_t lc, uint32_t c,
+                                                   uint32_t base, uint32_t boff, const u32x4* slot,
+                                                   uint32_t* scratch) const {
+        uint32_t lane = lane_id();
+        asm volatile("" : "+v"(lane));
+        for (uint32_t t = 0; t < lc; ++t) scratch[excl + t] = (lane << 8) | t;
+        const uint32_t ent = lane < c ? scratch[lane] : 0u;
+        const uint32_t src = ent >> 8, rank = ent & 255u;
+        // every lane takes part in the permute (a lane outside it would not
+        // provide its mask)
+        uint32_t mm = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(src << 2), (int)m);
+        uint32_t key = 0;
+        if (lane < c) {
+            // position of the set bit of that rank (from bit 0)
+            uint32_t e = 0, rr = rank;
+#pragma unroll
+            for (int wdt = 16; wdt >= 1; wdt >>= 1) {
+                const uint32_t low = (uint32_t)__builtin_popcount(mm & ((1u << wdt) - 1u));
+                if (rr >= low) {
+                    rr -= low;
+                    mm >>= wdt;
+                    e += wdt;
+                }
+            }
+            const uint32_t u = e / V, q = e % V;
+            const unsigned char* p = reinterpret_cast<const unsigned char*>(slot + u * 64 + src) + q * D::kBytes;
+            const uint32_t raw = D::kBytes == 4 ? *reinterpret_cast<const uint32_t*>(p)
+                                                : (uint32_t)*reinterpret_cast<const uint16_t*>(p);
+            key = D::key(raw);
+            s.keys[base + lane] = (typename D::Key)key;
+            s.idx[base + lane] = part_elem0 + boff + u * UE + src * V + q;
+        }
+        publish_max(s.misc, key);  // every lane takes part in the reduction
+    }
+
+    // Append a whole full block at pos (before the first compaction, when
+    // pos is a multiple of 8): lane l's U*V elements go to pos + l*U*V in its
+    // element order with 16-byte stores, keys transformed a 32-bit word at a
+    // time.
+    __device__ __forceinline__ void append_full(const BlockRegs<U>& r, uint32_t pos, uint32_t boff) const {
+        uint32_t lane = lane_id();
+        asm volatile("" : "+v"(lane));  // nothing here may be hoisted out of the retry loop
+        const uint32_t at0 = pos + lane * (U * V);
+        const uint32_t col0 = part_elem0 + boff + lane * V;
+        uint32_t kmax = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t at = at0 + u * V;
+            u32x4 kw;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t d = r.v[u][q];
+                uint32_t key;
+                if constexpr (D::kBytes == 4) {
+                    key = key_f32(d);
+                    kmax = key > kmax ? key : kmax;
+                } else {
+                    // both halves: flip every bit of a negative pattern, the sign bit otherwise
+                    const uint32_t neg = ((d >> 15) & 0x00010001u) * 0xFFFFu;
+                    key = d ^ (neg | 0x80008000u);
+                    const uint32_t lo = key & 0xFFFFu, hi = key >> 16;
+                    const uint32_t m = lo > hi ? lo : hi;
+                    kmax = m > kmax ? m : kmax;
+                }
+                kw[q] = key;
+            }
+            *reinterpret_cast<u32x4*>(&s.keys[at]) = kw;
+            const uint32_t c = col0 + u * UE;
+#pragma unroll
+            for (int h = 0; h < V / 4; ++h)
+                *reinterpret_cast<u32x4*>(&s.idx[at + 4 * h]) = u32x4{c + 4 * h, c + 4 * h + 1, c + 4 * h + 2, c + 4 * h + 3};
         }
         publish_max(s.misc, kmax);
     }
@@ -544,7 +688,7 @@ struct RingStreamer {
     // appended in order up to (and including) the first block after which the
     // buffer holds k + B2 or more. Returns that block's wave, or -1.
     __device__ __forceinline__ int32_t append_from(const BlockRegs<U>& r0, uint32_t boff, uint32_t blen,
-                                                   int32_t first, int32_t nblk) {
+                                                   int32_t first, int32_t nblk, const u32x4* slot) {
         // The block passes through an empty asm statement here, so nothing
         // derived from it (keys, shifted words, columns of every slot) can be
         // hoisted out of the step's retry loop and held in registers.
@@ -553,14 +697,15 @@ struct RingStreamer {
         for (int u = 0; u < U; ++u) asm volatile("" : "+v"(r.v[u]));
         const int w = wave_id();
         const bool mine = w >= first && w < nblk;
-        uint32_t lc = 0;
+        uint32_t lc = 0, lm = 0;
         Thresh th{};
         if (mine) {
             if (!st.tset) {
                 lc = lane_valid(blen);
             } else {
                 th = make_thresh<D>(st.tkey);
-                lc = th.neg ? lane_above<true>(r, th.thr) : lane_above<false>(r, th.thr);
+                lm = th.neg ? lane_mask<true>(r, th.thr) : lane_mask<false>(r, th.thr);
+                lc = mask_count(lm);
             }
         }
         const uint32_t incl = wave_prefix_sum(lc);
@@ -585,12 +730,18 @@ struct RingStreamer {
         const int32_t last = trig >= 0 ? trig : nblk - 1;
         if (mine && w <= last && c != 0) {
             const uint32_t pos = my_base + incl - lc;
-            if (!st.tset)
-                scatter<0>(r, pos, boff, blen, 0u);
-            else if (th.neg)
-                scatter<2>(r, pos, boff, blen, th.thr);
-            else
-                scatter<1>(r, pos, boff, blen, th.thr);
+            if (!st.tset) {
+                if (blen == (uint32_t)(U * UE) && (my_base & 7u) == 0u)
+                    append_full(r, my_base, boff);
+                else
+                    scatter_valid(r, pos, boff, blen);
+            } else if (kMasks && c <= 64u) {
+                scatter_sparse(lm, incl - lc, lc, c, my_base, boff, slot, s.sparse + w * 64);
+            } else if (kMasks) {
+                scatter_dense(r, lm, pos, boff);
+            } else {
+                scatter_dense(r, th.neg ? lane_bits<true>(r, th.thr) : lane_bits<false>(r, th.thr), pos, boff);
+            }
         }
         st.A += run - st.len;
         st.maxlen = run > st.maxlen ? run : st.maxlen;
@@ -598,10 +749,27 @@ struct RingStreamer {
         return trig;
     }
 
+    // Per-element admission as a 64-bit mask when a lane holds more than 32
+    // elements (the dense scatter then tests bits of it).
+    template <bool kNeg>
+    __device__ __forceinline__ uint64_t lane_bits(const BlockRegs<U>& r, uint32_t thr) const {
+        uint64_t m = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int q = 0; q < V; ++q) m |= above_k<kNeg>(test_word<D, U>(r, u, q), thr) ? 1ull << (u * V + q) : 0ull;
+        }
+        return m;
+    }
+
     __device__ __forceinline__ void run() {
         const int w = wave_id();
+        // Only the first block is requested before the loop: with every
+        // workgroup starting at once, the first blocks then come back without
+        // queueing behind everyone's later ones. The rest of the ring is
+        // requested as soon as the first block has landed.
         int32_t issued = 0;  // steps whose block of this wave is fetched
-        for (; issued < depth && issued < nsteps; ++issued) fetch(issued * NW + w, issued);
+        if (nsteps > 0) fetch(w, 0), issued = 1;
         BlockRegs<U> r;
         for (int32_t stp = 0; stp < nsteps; ++stp) {
             const int32_t q = stp % depth;
@@ -610,10 +778,13 @@ struct RingStreamer {
             block_at(stp * NW + w, boff, blen);
             wait_block(issued - 1 - stp);
             read_slot(q, r);
+            if (stp == 0) {
+                for (; issued < depth && issued < nsteps; ++issued) fetch(issued * NW + w, issued);
+            }
             if (w < nblk && blen != U * UE) mask_tail(r, blen);
             int32_t first = 0;
             while (true) {
-                const int32_t trig = append_from(r, boff, blen, first, nblk);
+                const int32_t trig = append_from(r, boff, blen, first, nblk, ring + q * U * 64);
                 if (trig < 0) break;
                 compact<D, NW>(s, st, k);
                 if (trig >= nblk - 1) break;

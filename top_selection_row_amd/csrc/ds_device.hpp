@@ -287,18 +287,26 @@ __device__ __forceinline__ void hist_pass(const typename D::Key* keys, uint32_t 
 template <int NW>
 __device__ __forceinline__ void fold_pass(uint32_t* hist, uint32_t* folded) {
     constexpr int NT = NW * 64;
-    constexpr int WPT = kHistWords / NT;      // words per thread (4 or 8)
-    constexpr int TPG = kHistCopies / WPT;    // threads per group (4 or 2)
-    static_assert(WPT % 4 == 0 && TPG >= 1, "fold split");
+    constexpr int WPT = kHistWords / NT;      // words per thread (2, 4 or 8)
+    constexpr int TPG = kHistCopies / WPT;    // threads per group (8, 4 or 2)
+    static_assert((WPT == 2 || WPT % 4 == 0) && TPG >= 1 && TPG <= 8, "fold split");
     const int t = threadIdx.x, g = t / TPG;
-    u32x4* h = reinterpret_cast<u32x4*>(hist) + t * (WPT / 4);
     uint32_t a = 0, b = 0;
+    if constexpr (WPT == 2) {
+        uint2* h = reinterpret_cast<uint2*>(hist) + t;
+        const uint2 v = *h;
+        a = (v.x & 0xFFFFu) + (v.y & 0xFFFFu);
+        b = (v.x >> 16) + (v.y >> 16);
+        *h = uint2{0u, 0u};
+    } else {
+        u32x4* h = reinterpret_cast<u32x4*>(hist) + t * (WPT / 4);
 #pragma unroll
-    for (int j = 0; j < WPT / 4; ++j) {
-        const u32x4 v = h[j];
-        a += (v.x & 0xFFFFu) + (v.y & 0xFFFFu) + (v.z & 0xFFFFu) + (v.w & 0xFFFFu);
-        b += (v.x >> 16) + (v.y >> 16) + (v.z >> 16) + (v.w >> 16);
-        h[j] = u32x4{0u, 0u, 0u, 0u};
+        for (int j = 0; j < WPT / 4; ++j) {
+            const u32x4 v = h[j];
+            a += (v.x & 0xFFFFu) + (v.y & 0xFFFFu) + (v.z & 0xFFFFu) + (v.w & 0xFFFFu);
+            b += (v.x >> 16) + (v.y >> 16) + (v.z >> 16) + (v.w >> 16);
+            h[j] = u32x4{0u, 0u, 0u, 0u};
+        }
     }
     if constexpr (TPG >= 2) {
         a += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x111, 0xF, 0xF, true);
@@ -308,14 +316,19 @@ __device__ __forceinline__ void fold_pass(uint32_t* hist, uint32_t* folded) {
         a += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x112, 0xF, 0xF, true);
         b += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b, 0x112, 0xF, 0xF, true);
     }
+    if constexpr (TPG >= 8) {
+        a += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x114, 0xF, 0xF, true);
+        b += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b, 0x114, 0xF, 0xF, true);
+    }
     if (t % TPG == TPG - 1) reinterpret_cast<uint2*>(folded)[g] = uint2{a, b};
 }
 
 // The bin of folded[256] that holds the rank-th largest key (every wave, same
 // answer): lane l takes bins 4*(63-l) .. 4*(63-l)+3, a prefix sum over lanes
 // counts the keys from the top bin down, the first lane reaching rank names
-// the group and a 4-bin step the bin. rank becomes the rank inside that bin.
-__device__ __forceinline__ uint32_t pick_bin(const uint32_t* folded, uint32_t& rank) {
+// the group and a 4-bin step the bin. rank becomes the rank inside that bin,
+// count the number of keys in it.
+__device__ __forceinline__ uint32_t pick_bin(const uint32_t* folded, uint32_t& rank, uint32_t& count) {
     const int lane = lane_id();
     const u32x4 c = reinterpret_cast<const u32x4*>(folded)[63 - lane];
     const uint32_t s = c.x + c.y + c.z + c.w;
@@ -327,18 +340,23 @@ __device__ __forceinline__ uint32_t pick_bin(const uint32_t* folded, uint32_t& r
     const uint32_t c3 = uniform(__builtin_amdgcn_readlane(c.w, L));
     const uint32_t c2 = uniform(__builtin_amdgcn_readlane(c.z, L));
     const uint32_t c1 = uniform(__builtin_amdgcn_readlane(c.y, L));
+    const uint32_t c0 = uniform(__builtin_amdgcn_readlane(c.x, L));
     uint32_t d;
     if (above_cnt + c3 >= rank) {
         d = 4u * g + 3u;
+        count = c3;
     } else if (above_cnt + c3 + c2 >= rank) {
         above_cnt += c3;
         d = 4u * g + 2u;
+        count = c2;
     } else if (above_cnt + c3 + c2 + c1 >= rank) {
         above_cnt += c3 + c2;
         d = 4u * g + 1u;
+        count = c1;
     } else {
         above_cnt += c3 + c2 + c1;
         d = 4u * g;
+        count = c0;
     }
     rank -= above_cnt;
     return d;
@@ -451,6 +469,70 @@ __device__ __forceinline__ void partition_keep(typename D::Key* keys, uint32_t* 
     }
 }
 
+// The rest of a select once the bin of the k-th key holds few keys: every
+// key of keys[0, n) with key - base <= span is appended to gathered[] (a
+// counter in *gcount, zero on entry), then after one barrier every wave
+// resolves the remaining digits of the gathered keys alone, on its own
+// 256-bin histogram (a quarter of the histogram copies, clear on entry and
+// on return): no further barrier and no fold.
+template <class D, int NW>
+__device__ __forceinline__ uint32_t finish_gathered(const typename D::Key* keys, uint32_t n, uint32_t base,
+                                                    uint32_t span, int s, uint32_t& rank, uint32_t* hist,
+                                                    uint32_t* gathered, uint32_t* gcount) {
+    constexpr uint32_t NT = NW * 64;
+    const uint32_t nch = (n + kChunk - 1) / kChunk;
+    const int lane0 = lane_id();
+    for (uint32_t c0 = 0; c0 < nch; c0 += NT) {
+        const uint32_t c = c0 + threadIdx.x;
+        KeyChunk<D> kc;
+        read_chunk<D>(kc, keys, c < nch ? c : 0u);
+        const uint32_t lim = c < nch ? n - c * kChunk : 0u;
+        uint32_t m = 0;  // entries of this chunk in the window
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i)
+            m |= ((uint32_t)i < lim && chunk_key<D>(kc, i) - base <= span) ? 1u << i : 0u;
+        // one counter update per wave: a lane prefix sum of the matches, the
+        // last lane reserves the wave's slots
+        const uint32_t cnt = (uint32_t)__builtin_popcount(m);
+        const uint32_t incl = wave_prefix_sum(cnt);
+        const uint32_t total = uniform(__builtin_amdgcn_readlane(incl, 63));
+        if (total != 0u) {
+            uint32_t at = 0;
+            if (lane0 == 63) at = atomicAdd(gcount, total);
+            at = uniform(__builtin_amdgcn_readlane(at, 63)) + incl - cnt;
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                if ((m >> i) & 1u) {
+                    if (at < (uint32_t)kGather) gathered[at] = chunk_key<D>(kc, i);
+                    ++at;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t ng = min(uniform(*gcount), (uint32_t)kGather);
+    const int lane = lane_id();
+    uint32_t g[kGather / 64];
+#pragma unroll
+    for (int j = 0; j < kGather / 64; ++j) g[j] = (uint32_t)(lane + 64 * j) < ng ? gathered[lane + 64 * j] : 0u;
+    static_assert(NW * 256 <= (int)kHistWords, "a 256-bin histogram per wave must fit the histogram copies");
+    uint32_t* wh = hist + wave_id() * 256;  // this wave's 256 bins
+    while (s > 0) {
+        s = s > 8 ? s - 8 : 0;
+#pragma unroll
+        for (int j = 0; j < kGather / 64; ++j) {
+            const uint32_t u = g[j] - base;
+            if ((uint32_t)(lane + 64 * j) < ng && u <= span) atomicAdd(&wh[(u >> s) & 255u], 1u);
+        }
+        uint32_t cnt;
+        const uint32_t d = pick_bin(wh, rank, cnt);
+        reinterpret_cast<u32x4*>(wh)[lane] = u32x4{0u, 0u, 0u, 0u};
+        base += d << s;
+        span = (1u << s) - 1u;
+    }
+    return base;
+}
+
 // RadixSelectTopK: keep the k largest of keys/idx[0, n) (k <= n) in [0, k)
 // and return the k-th largest key. Every key lies in [lo, hi]. Entries
 // [junk, junk+64) of both arrays are scratch for dropped entries. Starts with a
@@ -458,19 +540,26 @@ __device__ __forceinline__ void partition_keep(typename D::Key* keys, uint32_t* 
 // clear on entry and are clear on return.
 template <class D, int NW>
 __device__ uint32_t select_topk(typename D::Key* keys, uint32_t* idx, uint32_t* hist, uint32_t* folded,
-                                uint32_t* tot, uint32_t junk, uint32_t n, uint32_t k, uint32_t lo, uint32_t hi) {
+                                uint32_t* tot, uint32_t* gathered, uint32_t* gcount, uint32_t junk, uint32_t n,
+                                uint32_t k, uint32_t lo, uint32_t hi) {
     __syncthreads();
     uint32_t base = lo, span = hi - lo, rank = k;
     int s = span ? 32 - __clz(span) : 0;  // bit length of the span
     s = s > 8 ? s - 8 : 0;
     while (true) {
         hist_pass<D, NW>(keys, n, base, span, s, hist);
+        if (threadIdx.x == 0) *gcount = 0u;
         __syncthreads();
         fold_pass<NW>(hist, folded);
         __syncthreads();
-        base += pick_bin(folded, rank) << s;
+        uint32_t cnt;
+        base += pick_bin(folded, rank, cnt) << s;
         if (s == 0) break;
         span = (1u << s) - 1u;
+        if (cnt <= (uint32_t)kGather) {
+            base = finish_gathered<D, NW>(keys, n, base, span, s, rank, hist, gathered, gcount);
+            break;
+        }
         s = s > 8 ? s - 8 : 0;
     }
     partition_keep<D, NW>(keys, idx, tot, n, base, rank, junk);

@@ -26,6 +26,7 @@ constexpr size_t kLdsLimit = 160 * 1024;  // gfx950 LDS per workgroup
 constexpr int64_t kPartBytesMax = (int64_t)1 << 31;  // 32-bit buffer offsets per part
 constexpr int kChunk = 8;                 // candidate entries per thread and select round
 constexpr int kRoundsPerGroup = 2;        // select rounds whose entries a thread holds at once
+constexpr int kGather = 256;              // radix bins this small are finished by every wave alone
 
 DS_HD inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 DS_HD inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -57,6 +58,8 @@ struct Layout {
     uint32_t idx;    // cap candidate column indices (uint32), the same padding and junk
     uint32_t hist;   // radix histogram: 16 copies of 256 16-bit counters (8 KiB)
     uint32_t fold;   // 256 folded bins (uint32)
+    uint32_t gather; // kGather keys of one radix bin (uint32), gathered for a wave-local finish
+    uint32_t sparse; // 64 uint32 per wave: survivor list of a wave with few survivors
     uint32_t tot;    // 2 x rounds x waves per-wave totals of the select partition
     uint32_t cnt;    // 2 x waves per-wave counts (block loop)
     uint32_t perm;   // block order (uint16 per block)
@@ -91,6 +94,10 @@ inline Layout make_layout_raw(int key_bytes, int64_t cap, int64_t order_n, int w
     off += (size_t)16 * 128 * 4;
     L.fold = (uint32_t)off;
     off += 256 * 4;
+    L.gather = (uint32_t)off;
+    off += kGather * 4;
+    L.sparse = (uint32_t)off;
+    off += (size_t)waves * 64 * 4;
     L.tot = (uint32_t)off;
     off += align_up((size_t)2 * kRoundsPerGroup * waves * 4, 16);
     L.cnt = (uint32_t)off;
