@@ -1265,19 +1265,27 @@ static bool lds_fits(int dtype, int64_t n, int64_t k, int64_t B, int64_t B2, int
 
 static int plan_split(int dtype, int64_t batch, int64_t n, int32_t k, int32_t B, int32_t B2, int32_t num_cus) {
     const int64_t lo = split_lower_bound(dtype, n, B);
+    // Split when the rows fill at most half the compute units, about one
+    // part per unit; no more parts than keep the streamed bytes of a part
+    // ahead of its k results (sqrt(N*size / 8k)), no part shorter than two
+    // steps of 8 blocks, and at most kSplitPlanMax parts (the merge grows
+    // with their number).
+    constexpr int64_t kSplitPlanMax = 16;
     int64_t S = 1;
-    if (batch > 0 && batch < num_cus / 2) S = ceil_div(num_cus, batch);
+    if (batch > 0 && batch <= num_cus / 2) S = ceil_div(num_cus, batch);
     const double bal = std::floor(std::sqrt((double)n * elem_bytes(dtype) / (8.0 * (double)k)));
     S = std::min<int64_t>(S, std::max<int64_t>(1, (int64_t)bal));
+    S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(n, B) / 16));
+    S = std::min<int64_t>(S, kSplitPlanMax);
     S = std::max<int64_t>(S, lo);
     while (S > lo && (!split_ok(n, k, B, S) || !lds_fits(dtype, n, k, B, B2, S, kGW))) --S;
     if (!split_ok(n, k, B, S) || !lds_fits(dtype, n, k, B, B2, S, kGW)) return DS_ERR_UNSUPPORTED;
     return (int)S;
 }
 
-// Waves per workgroup of the streaming kernel: 8 when the workgroups would
-// leave compute units idle, else 4.
-static int plan_waves(int64_t items, int32_t num_cus) { return items * 2 <= num_cus ? 8 : 4; }
+// Waves per workgroup of the streaming kernel: 8 while there is at most one
+// workgroup per compute unit, else 4.
+static int plan_waves(int64_t items, int32_t num_cus) { return items <= num_cus ? 8 : 4; }
 
 struct DevInfo {
     int cus = 0;
