@@ -17,9 +17,10 @@ Commands (each summary records the full command lines that produced it):
   python -m top_selection_row_amd.profiling traffic --workload W \
         --kernel-fetch DIR --kernel-write DIR --copy-fetch DIR --copy-write DIR \
         --copy-bytes N [--out FILE]
-      HBM bytes per launch of the DeepSelect kernel from FETCH_SIZE and
-      WRITE_SIZE, each scaled by what the same counter reads for a plain copy
-      kernel of known size (bytes read = bytes written = N per copy).
+      HBM bytes per call (the DeepSelect kernels of one call summed) from
+      FETCH_SIZE and WRITE_SIZE, each scaled by what the same counter reads for
+      a plain copy kernel of known size (bytes read = bytes written = N per
+      copy).
 """
 from __future__ import annotations
 
@@ -103,10 +104,13 @@ def cmd_trace(a):
         print(f"{short(r['Name'])[:70]:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
               f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}")
     if a.match:
-        ds = kernel_durations(a.dir, a.match)
-        if ds:
-            print(f"# {a.match}: {len(ds)} dispatches, mean {statistics.fmean(ds) / 1e3:.2f} us, "
-                  f"median {statistics.median(ds) / 1e3:.2f} us")
+        # one call runs each matching kernel once (the part kernel, plus the
+        # merge kernel when rows are split): the per-call time is their sum
+        per = [(short(r["Name"]), float(r["AverageNs"]) / 1e3) for r in rows if a.match in r["Name"]]
+        if per:
+            total = sum(v for _, v in per)
+            print(f"# per call ({' + '.join(n.split('<')[0].split('::')[-1] for n, _ in per)}): "
+                  f"{total:.2f} us (sum of the kernel averages)")
 
 
 def cmd_counters(a):
@@ -143,14 +147,16 @@ def cmd_traffic(a):
     for k, cs in kw.items():
         if "WRITE_SIZE" in cs:
             kern.setdefault(k, {})["write_bytes"] = cs["WRITE_SIZE"] * 1024.0 * w_scale
-    main = max(kern.items(), key=lambda kv: kv[1].get("fetch_bytes", 0.0))
+    # a call launches each DeepSelect kernel once: per-call bytes are the sum
+    fetch = sum(v.get("fetch_bytes", 0.0) for v in kern.values())
+    write = sum(v.get("write_bytes", 0.0) for v in kern.values())
     out = {
         "workload": a.workload,
         "source_digest": source_digest(),
-        "kernel": main[0],
-        "fetch_bytes_per_launch": main[1].get("fetch_bytes"),
-        "write_bytes_per_launch": main[1].get("write_bytes"),
-        "hbm_bytes_per_launch": main[1].get("fetch_bytes", 0.0) + main[1].get("write_bytes", 0.0),
+        "kernels": sorted(kern),
+        "fetch_bytes_per_launch": fetch,
+        "write_bytes_per_launch": write,
+        "hbm_bytes_per_launch": fetch + write,
         "copy_calibration": {"copy_bytes": a.copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale},
         "all_kernels": kern,
         "commands": a.cmd,
