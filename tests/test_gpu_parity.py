@@ -247,7 +247,8 @@ def test_caller_workspace():
     xt = to_device(x)
     S = 4
     nbytes = ds.deepselect_workspace_bytes(ds.DS_F32, 16, w.n, w.k, w.block, w.block2, S)
-    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    # no initial contents are needed
+    ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=DEV)
     vals = torch.empty((16, w.k), dtype=torch.float32, device=DEV)
     idx = torch.empty((16, w.k), dtype=torch.int32, device=DEV)
     stream = torch.cuda.current_stream().cuda_stream
@@ -263,3 +264,15 @@ def test_caller_workspace():
                                vals.data_ptr(), idx.data_ptr(), stream, split=S,
                                workspace=ws.data_ptr(), workspace_bytes=nbytes - 1)
     assert rc == ds.DS_ERR_WORKSPACE
+
+
+def test_library_workspace_across_shapes():
+    # split calls of changing batch and split on one stream share its library
+    # workspace: grown, reused by a smaller shape, and reused again
+    w = synth.WORKLOADS["dsa32k"]
+    x = synth.generate("dsa32k")
+    for batch, S in [(16, 4), (64, 2), (8, 8), (64, 4), (32, 2), (64, 2), (64, 2)]:
+        log(f"[gpu] library workspace: batch {batch} split {S}")
+        vals, idx, st = run_gpu(x[:batch], w.k, w.block, w.block2, split=S)
+        check_rows(x[:batch], vals, idx, w.k)
+        check_stats_against_model(x[:batch], st, w.k, w.block, w.block2, 0, S, range(2))

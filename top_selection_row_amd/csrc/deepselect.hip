@@ -1139,72 +1139,95 @@ __global__ __launch_bounds__(kGW * 64) void deepselect_generic_kernel(Params p) 
 }
 
 // ===========================================================================
-// Merge kernel of split rows: DeepSelect over the S part results of a row,
-// one block of k candidates per part, in the random order of tag 1.
+// Merge kernel of split rows: DeepSelect over the S part results of a row, one
+// block of k candidates per part, in the random order of tag 1. A tile is kMT
+// candidates per lane (lanes contiguous per load); the tile after the current
+// one is loaded while the current one is appended, so the loads of a row pay
+// the memory latency about once.
 // ===========================================================================
-template <class D>
-__global__ __launch_bounds__(kGW * 64) void deepselect_merge_kernel(Params p) {
+constexpr int kMT = 4;
+
+struct MergeTile {
+    uint32_t key[kMT], col[kMT];
+};
+
+template <int NW>
+__device__ __forceinline__ void load_merge_tile(MergeTile& t, const Params& p, const uint16_t* perm, int64_t row,
+                                                int64_t tile, uint32_t tiles_per_part) {
+    constexpr uint32_t TE = NW * 64 * kMT;
+    const uint32_t k = (uint32_t)p.k;
+    const int64_t i = tile / tiles_per_part;
+    const uint32_t t0 = (uint32_t)(tile - i * tiles_per_part) * TE;
+    const int64_t part = (int64_t)uniform(perm[i]);
+    const int64_t off = (row * p.split + part) * (int64_t)k + t0;
+#pragma unroll
+    for (int q = 0; q < kMT; ++q) {
+        const uint32_t e = (uint32_t)q * NW * 64 + (uint32_t)threadIdx.x;
+        const bool inb = t0 + e < k;
+        t.key[q] = inb ? p.ws_keys[off + e] : 0u;
+        t.col[q] = inb ? p.ws_idx[off + e] : 0u;
+    }
+}
+
+template <class D, int NW>
+__global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     Lds<D> s = lds_of<D>(smem, p.L);
+    constexpr uint32_t TE = NW * 64 * kMT;
     const uint32_t k = (uint32_t)p.k, B2 = (uint32_t)p.B2;
     const int32_t S = p.split;
-    constexpr uint32_t kTE = kGW * 64 * 4;
+    const uint32_t tpp = (k + TE - 1) / TE;  // tiles per part
+    const int64_t tiles = (int64_t)S * tpp;
     for (int64_t row = blockIdx.x; row < p.batch; row += gridDim.x) {
-        __syncthreads();
-        begin_item<D, kGW>(s);
-        build_order<kGW>(s.perm, p.seed, row, 1, 0, S, s.base);
+        __syncthreads();  // LDS free from the previous row
+        begin_item<D, NW>(s);
+        build_order<NW>(s.perm, p.seed, row, 1, 0, S, s.base);
         RunState st;
-        for (int32_t i = 0; i < S; ++i) {
-            const int64_t part = (int64_t)uniform(s.perm[i]);
-            const uint32_t* wk = p.ws_keys + (row * S + part) * (int64_t)k;
-            const uint32_t* wi = p.ws_idx + (row * S + part) * (int64_t)k;
-            for (uint32_t t0 = 0; t0 < k; t0 += kTE) {
-                const uint32_t tv = (k - t0) < kTE ? (k - t0) : kTE;
-                uint32_t kk[4], ii[4];
-                bool inb[4];
+        MergeTile cur, nxt;
+        load_merge_tile<NW>(cur, p, s.perm, row, 0, tpp);
+        for (int64_t j = 0; j < tiles; ++j) {
+            if (j + 1 < tiles) load_merge_tile<NW>(nxt, p, s.perm, row, j + 1, tpp);
+            const uint32_t t0 = (uint32_t)(j % tpp) * TE;
+            const uint32_t tv = (k - t0) < TE ? (k - t0) : TE;
+            uint32_t kmax = 0;
+            if (!st.tset) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t e = (uint32_t)threadIdx.x * 4u + (uint32_t)q;
-                    inb[q] = e < tv;
-                    kk[q] = inb[q] ? wk[t0 + e] : 0u;
-                    ii[q] = inb[q] ? wi[t0 + e] : 0u;
-                }
-                uint32_t kmax = 0;
-                if (!st.tset) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        if (inb[q]) {
-                            const uint32_t pos = st.len + (uint32_t)threadIdx.x * 4u + (uint32_t)q;
-                            s.keys[pos] = (typename D::Key)kk[q];
-                            s.idx[pos] = ii[q];
-                            kmax = kk[q] > kmax ? kk[q] : kmax;
-                        }
+                for (int q = 0; q < kMT; ++q) {
+                    const uint32_t e = (uint32_t)q * NW * 64 + (uint32_t)threadIdx.x;
+                    if (e < tv) {
+                        s.keys[st.len + e] = (typename D::Key)cur.key[q];
+                        s.idx[st.len + e] = cur.col[q];
+                        kmax = cur.key[q] > kmax ? cur.key[q] : kmax;
                     }
-                    st.len += tv;
-                    st.A += tv;
-                } else {
-                    bool pred[4];
-                    uint64_t masks[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        pred[q] = inb[q] && kk[q] > st.tkey;
-                        masks[q] = __ballot(pred[q]);
-                    }
-                    const uint32_t added = append_masked<kGW, 4>(masks, pred, st.len, s.cnt, st.par,
-                                                                 [&](int q, uint32_t pos) {
-                                                                     s.keys[pos] = (typename D::Key)kk[q];
-                                                                     s.idx[pos] = ii[q];
-                                                                     kmax = kk[q] > kmax ? kk[q] : kmax;
-                                                                 });
-                    st.len += added;
-                    st.A += added;
                 }
-                publish_max(s.misc, kmax);
+                st.len += tv;
+                st.A += tv;
+            } else {
+                bool pred[kMT];
+                uint64_t masks[kMT];
+#pragma unroll
+                for (int q = 0; q < kMT; ++q) {
+                    const uint32_t e = (uint32_t)q * NW * 64 + (uint32_t)threadIdx.x;
+                    pred[q] = e < tv && cur.key[q] > st.tkey;
+                    masks[q] = __ballot(pred[q]);
+                }
+                const uint32_t added =
+                    append_masked<NW, kMT>(masks, pred, st.len, s.cnt, st.par, [&](int q, uint32_t pos) {
+                        s.keys[pos] = (typename D::Key)cur.key[q];
+                        s.idx[pos] = cur.col[q];
+                        kmax = cur.key[q] > kmax ? cur.key[q] : kmax;
+                    });
+                st.len += added;
+                st.A += added;
             }
-            st.maxlen = st.len > st.maxlen ? st.len : st.maxlen;
-            if (st.len >= k + B2) compact<D, kGW>(s, st, k);
+            publish_max(s.misc, kmax);
+            if ((j + 1) % tpp == 0) {  // a part's block ends: the compaction check
+                st.maxlen = st.len > st.maxlen ? st.len : st.maxlen;
+                if (st.len >= k + B2) compact<D, NW>(s, st, k);
+            }
+            cur = nxt;
         }
-        final_select<D, kGW>(s, st, k);
+        final_select<D, NW>(s, st, k);
         uint64_t W = st.W, A = st.A, R = st.R, maxlen = st.maxlen;
         for (int32_t q = 0; q < S; ++q) {
             const uint64_t* o = p.ws_stats + (row * S + q) * DS_STATS_PER_ROW;
@@ -1213,7 +1236,7 @@ __global__ __launch_bounds__(kGW * 64) void deepselect_merge_kernel(Params p) {
             R += o[DS_STAT_R];
             maxlen = o[DS_STAT_MAX_LEN] > maxlen ? o[DS_STAT_MAX_LEN] : maxlen;
         }
-        write_row<D, kGW>(s, p, row, W, A, R, maxlen);
+        write_row<D, NW>(s, p, row, W, A, R, maxlen);
     }
 }
 
@@ -1390,9 +1413,15 @@ static int launch_all(KernelKind kind, int units, int waves, bool vec, Params pr
     else
         rc = launch_kernel(deepselect_generic_kernel<D, false>, items, kGW * 64, lds, st, prm);
     if (rc != DS_OK || prm.split == 1) return rc;
+    // the merge runs on 8 waves when their layout fits, else on 4
     const int dtype = D::kBytes == 4 ? DS_F32 : DS_BF16;
+    const Layout M8 = make_merge_layout(dtype, prm.k, prm.B2, prm.split, 8);
+    if (M8.total <= kLdsLimit) {
+        prm.L = M8;
+        return launch_kernel(deepselect_merge_kernel<D, 8>, prm.batch, 8 * 64, prm.L.total, st, prm);
+    }
     prm.L = make_merge_layout(dtype, prm.k, prm.B2, prm.split, kGW);
-    return launch_kernel(deepselect_merge_kernel<D>, prm.batch, kGW * 64, prm.L.total, st, prm);
+    return launch_kernel(deepselect_merge_kernel<D, kGW>, prm.batch, kGW * 64, prm.L.total, st, prm);
 }
 
 static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int32_t B,

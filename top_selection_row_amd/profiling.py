@@ -104,13 +104,15 @@ def cmd_trace(a):
         print(f"{short(r['Name'])[:70]:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
               f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}")
     if a.match:
-        # one call runs each matching kernel once (the part kernel, plus the
-        # merge kernel when rows are split): the per-call time is their sum
-        per = [(short(r["Name"]), float(r["AverageNs"]) / 1e3) for r in rows if a.match in r["Name"]]
+        # a call runs the part kernel once, plus the merge kernel when rows are
+        # split: the per-call time is the matching kernels' total over the calls
+        per = [(short(r["Name"]), float(r["TotalDurationNs"]) / 1e3, int(r["Calls"]))
+               for r in rows if a.match in r["Name"]]
         if per:
-            total = sum(v for _, v in per)
-            print(f"# per call ({' + '.join(n.split('<')[0].split('::')[-1] for n, _ in per)}): "
-                  f"{total:.2f} us (sum of the kernel averages)")
+            calls = max(c for _, _, c in per)
+            total = sum(t for _, t, _ in per) / calls
+            print(f"# per call ({' + '.join(n.split('<')[0].split('::')[-1] for n, _, _ in per)}, "
+                  f"{calls} calls): {total:.2f} us (total duration / calls)")
 
 
 def cmd_counters(a):
