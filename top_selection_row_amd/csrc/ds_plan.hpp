@@ -122,7 +122,9 @@ inline Layout make_layout(int dtype, int64_t n, int64_t k, int64_t B, int64_t B2
 // Add a streaming ring to a layout: every wave gets `depth` slots of `units`
 // KiB, depth as large as LDS allows up to kRingMax (and no more than the steps
 // of a part). Leaves the layout without a ring when fewer than 2 slots fit.
-constexpr int kRingMax = 4;
+// Two slots (one block landing while the wave works on the other) measured as
+// fast as or faster than three or four on every workload here.
+constexpr int kRingMax = 2;
 inline Layout with_ring(Layout L, int64_t steps, int units, size_t lds_limit) {
     const size_t base = align_up(L.total, 16);
     const size_t per = (size_t)L.waves * units * kUnitBytes;
