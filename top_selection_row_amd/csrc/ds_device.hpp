@@ -364,14 +364,15 @@ __device__ __forceinline__ uint32_t pick_bin(const uint32_t* folded, uint32_t& r
 
 // Stable in-place partition of keys/idx[0, n): keep every key > kth and the
 // first `need` keys == kth, in buffer order, packed into [0, k). Groups of up
-// to kRoundsPerGroup rounds: every thread counts the greater and tied entries
-// of its chunks (low and high 16 bits of one word), a DPP prefix sum inside
-// the wave and one LDS exchange of the wave totals (one barrier per group)
-// give each chunk the number of kept entries before it, and a second walk
-// over the chunk stores the kept entries there. A destination never passes
-// the entry's own position, so no group overwrites an entry a later group
-// still reads. Dropped entries are stored to a per-lane junk slot past the
-// buffer, so the stores need no branch.
+// to kRoundsPerGroup rounds: every thread marks the greater and the tied
+// entries of its chunks in two 8-bit masks, a DPP prefix sum of their counts
+// inside the wave and one LDS exchange of the wave totals (one barrier per
+// group) give each chunk the number of kept entries before it, and each kept
+// entry goes to that number plus the kept entries before it in the chunk (a
+// bit count of the mask). A destination never passes the entry's own
+// position, so no group overwrites an entry a later group still reads.
+// Dropped entries are stored to a per-lane junk slot past the buffer, so the
+// stores need no branch.
 template <class D, int NW>
 __device__ __forceinline__ void partition_keep(typename D::Key* keys, uint32_t* idx, uint32_t* tot, uint32_t n,
                                                uint32_t kth, uint32_t need, uint32_t junk) {
@@ -381,10 +382,10 @@ __device__ __forceinline__ void partition_keep(typename D::Key* keys, uint32_t* 
     const uint32_t my_junk = junk + (uint32_t)lane;
     uint32_t run = 0, par = 0;  // greater | tied << 16 before this group
     for (uint32_t c0 = 0; c0 < nch; c0 += NT * R) {
-        const int nr = nch - c0 > (uint32_t)NT ? R : 1;  // rounds of this group holding chunks
+        const int nr = nch - c0 > (uint32_t)NT ? R : 1;
         KeyChunk<D> kc[R];
         u32x4 ix[R][2];
-        uint32_t lim[R], mine[R], incl[R];
+        uint32_t gm[R], em[R], mine[R], incl[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             if (r < nr) {
@@ -395,25 +396,18 @@ __device__ __forceinline__ void partition_keep(typename D::Key* keys, uint32_t* 
                 const u32x4* iv = reinterpret_cast<const u32x4*>(idx) + cr * 2u;
                 ix[r][0] = iv[0];
                 ix[r][1] = iv[1];
-                lim[r] = has ? n - c * kChunk : 0u;
+                const uint32_t lim = has ? n - c * kChunk : 0u;
+                const uint32_t valid = lim >= (uint32_t)kChunk ? 0xFFu : ((1u << lim) - 1u);
                 uint32_t g = 0, e = 0;
-                if (__ballot(lim[r] < (uint32_t)kChunk) == 0ull) {  // every chunk of the wave is full
 #pragma unroll
-                    for (int i = 0; i < kChunk; ++i) {
-                        const uint32_t key = chunk_key<D>(kc[r], i);
-                        g += key > kth ? 1u : 0u;
-                        e += key == kth ? 1u : 0u;
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < kChunk; ++i) {
-                        const uint32_t key = chunk_key<D>(kc[r], i);
-                        const bool v = (uint32_t)i < lim[r];
-                        g += (v && key > kth) ? 1u : 0u;
-                        e += (v && key == kth) ? 1u : 0u;
-                    }
+                for (int i = 0; i < kChunk; ++i) {
+                    const uint32_t key = chunk_key<D>(kc[r], i);
+                    g |= key > kth ? 1u << i : 0u;
+                    e |= key == kth ? 1u << i : 0u;
                 }
-                mine[r] = g | (e << 16);
+                gm[r] = g & valid;
+                em[r] = e & valid;
+                mine[r] = (uint32_t)__builtin_popcount(gm[r]) | ((uint32_t)__builtin_popcount(em[r]) << 16);
                 incl[r] = wave_prefix_sum(mine[r]);
                 if (lane == 63) tot[(par * R + r) * NW + wave] = incl[r];
             }
@@ -423,7 +417,7 @@ __device__ __forceinline__ void partition_keep(typename D::Key* keys, uint32_t* 
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             if (r < nr) {
-                uint32_t before = run, all = 0;  // packed counts before this wave / in this round
+                uint32_t before = run, all = 0;
 #pragma unroll
                 for (int w4 = 0; w4 < NW / 4; ++w4) {
                     const u32x4 x = tv[(r * NW) / 4 + w4];
@@ -434,33 +428,30 @@ __device__ __forceinline__ void partition_keep(typename D::Key* keys, uint32_t* 
                     }
                 }
                 const uint32_t excl = before + incl[r] - mine[r];
-                uint32_t tie = excl >> 16;
-                uint32_t dst = (excl & 0xFFFFu) + (tie < need ? tie : need);
-                if (__ballot(lim[r] < (uint32_t)kChunk) == 0ull) {
-#pragma unroll
-                    for (int i = 0; i < kChunk; ++i) {
-                        const uint32_t key = chunk_key<D>(kc[r], i);
-                        const bool eq = key == kth;
-                        const bool kp = key > kth || (eq && tie < need);
-                        const uint32_t at = kp ? dst : my_junk;
-                        keys[at] = (typename D::Key)key;
-                        idx[at] = ix[r][i >> 2][i & 3];
-                        dst += kp ? 1u : 0u;
-                        tie += eq ? 1u : 0u;
+                const uint32_t tie = excl >> 16;
+                const uint32_t ne = mine[r] >> 16;
+                // the tied entries of this chunk that are kept: the first
+                // need - tie of them (all when they fit, none when need is reached)
+                uint32_t ke = tie + ne <= need ? em[r] : 0u;
+                if (__ballot(tie < need && tie + ne > need) != 0ull) {
+                    if (tie < need && tie + ne > need) {
+                        uint32_t left = need - tie, m = em[r];
+                        for (int i = 0; i < kChunk; ++i) {
+                            if (left != 0u && ((m >> i) & 1u)) {
+                                ke |= 1u << i;
+                                --left;
+                            }
+                        }
                     }
-                } else {
+                }
+                const uint32_t km = gm[r] | ke;
+                const uint32_t dst0 = (excl & 0xFFFFu) + (tie < need ? tie : need);
 #pragma unroll
-                    for (int i = 0; i < kChunk; ++i) {
-                        const uint32_t key = chunk_key<D>(kc[r], i);
-                        const bool v = (uint32_t)i < lim[r];
-                        const bool eq = v && key == kth;
-                        const bool kp = (v && key > kth) || (eq && tie < need);
-                        const uint32_t at = kp ? dst : my_junk;
-                        keys[at] = (typename D::Key)key;
-                        idx[at] = ix[r][i >> 2][i & 3];
-                        dst += kp ? 1u : 0u;
-                        tie += eq ? 1u : 0u;
-                    }
+                for (int i = 0; i < kChunk; ++i) {
+                    const bool kp = (km >> i) & 1u;
+                    const uint32_t at = kp ? (uint32_t)__builtin_popcount(km & ((1u << i) - 1u)) + dst0 : my_junk;
+                    keys[at] = (typename D::Key)chunk_key<D>(kc[r], i);
+                    idx[at] = ix[r][i >> 2][i & 3];
                 }
                 run += all;
             }
