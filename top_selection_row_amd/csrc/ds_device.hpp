@@ -254,29 +254,39 @@ __device__ __forceinline__ void clear_words(uint32_t* p, uint32_t words) {
 }
 
 // Add every key of keys[0, n) with key - base <= span into the digit
-// (key - base) >> s of this lane's histogram copy. A key slot that no lane of
-// the wave counts is skipped (a uniform branch); otherwise every lane adds,
-// the ones that do not count add zero.
+// (key - base) >> s of this lane's histogram copy (16-bit counts, two bins a
+// word). Lanes whose key is outside the window do not add; a chunk's keys are
+// checked against the end of the buffer only in the round that holds it, and
+// the next round's chunk is read before this one is counted.
+template <class D, int NW, bool kFull>
+__device__ __forceinline__ void hist_chunk(const KeyChunk<D>& kc, uint32_t lim, uint32_t base, uint32_t span, int s,
+                                           uint32_t* hl) {
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+        const uint32_t u = chunk_key<D>(kc, i) - base;
+        if ((kFull || (uint32_t)i < lim) && u <= span)
+            atomicAdd(&hl[((u >> (s + 1)) & 127u) * kHistCopies], 1u + ((u >> s) & 1u) * 0xFFFFu);
+    }
+}
+
 template <class D, int NW>
 __device__ __forceinline__ void hist_pass(const typename D::Key* keys, uint32_t n, uint32_t base, uint32_t span,
                                           int s, uint32_t* hist) {
     constexpr uint32_t NT = NW * 64;
     const uint32_t nch = (n + kChunk - 1) / kChunk;
     uint32_t* hl = hist + (lane_id() & (kHistCopies - 1));
-    for (uint32_t c0 = 0; c0 < nch; c0 += NT) {
-        const uint32_t c = c0 + threadIdx.x;
-        KeyChunk<D> kc;
-        read_chunk<D>(kc, keys, c < nch ? c : 0u);
-        const uint32_t lim = c < nch ? n - c * kChunk : 0u;  // valid entries of this chunk
-#pragma unroll
-        for (int i = 0; i < kChunk; ++i) {
-            const uint32_t u = chunk_key<D>(kc, i) - base;
-            const bool ok = (uint32_t)i < lim && u <= span;
-            if (__ballot(ok) != 0ull) {
-                const uint32_t d = (u >> s) & 255u;
-                atomicAdd(&hl[(d >> 1) * kHistCopies], ok ? 1u << ((d & 1u) * 16) : 0u);
-            }
-        }
+    uint32_t c = threadIdx.x;
+    KeyChunk<D> kc;
+    read_chunk<D>(kc, keys, c < nch ? c : 0u);
+    for (uint32_t c0 = 0; c0 < nch; c0 += NT, c += NT) {
+        KeyChunk<D> nx = kc;
+        if (c0 + NT < nch) read_chunk<D>(nx, keys, c + NT < nch ? c + NT : 0u);  // the next round's chunk
+        const uint32_t lim = c < nch ? n - c * kChunk : 0u;
+        if (__ballot(lim < (uint32_t)kChunk) == 0ull)
+            hist_chunk<D, NW, true>(kc, lim, base, span, s, hl);
+        else
+            hist_chunk<D, NW, false>(kc, lim, base, span, s, hl);
+        kc = nx;
     }
 }
 
@@ -547,7 +557,9 @@ __device__ uint32_t select_topk(typename D::Key* keys, uint32_t* idx, uint32_t* 
         base += pick_bin(folded, rank, cnt) << s;
         if (s == 0) break;
         span = (1u << s) - 1u;
-        if (cnt <= (uint32_t)kGather) {
+        // gathering pays off when two or more digits remain (32-bit keys);
+        // for one more digit a plain pass is cheaper
+        if (cnt <= (uint32_t)kGather && s > 8) {
             base = finish_gathered<D, NW>(keys, n, base, span, s, rank, hist, gathered, gcount);
             break;
         }
