@@ -568,36 +568,42 @@ struct RingStreamer {
         publish_max(s.misc, kmax);
     }
 
-    // Append the lane's elements above T (mask m) at pos in element order.
-    // A slot no lane of the wave admits is skipped; otherwise the lanes that
-    // do not admit it store to their junk entry. The largest key appended is
-    // the block's largest key, since that one is admitted whenever any is.
-    template <class MaskT>
+    // Append the lane's elements above T (mask m) at pos in element order:
+    // element b of the lane goes to pos plus the number of admitted elements
+    // before it (a bit count of the mask), so the stores do not wait on each
+    // other; lanes that do not admit it store to their junk entry. With T at
+    // or above +0 (kPos) every admitted element is positive and its key is
+    // its bits with the sign bit set. The largest key appended is the block's
+    // largest key, since that one is admitted whenever any is.
+    template <bool kPos, class MaskT>
     __device__ __forceinline__ void scatter_dense(const BlockRegs<U>& r, MaskT m, uint32_t pos,
                                                   uint32_t boff) const {
         uint32_t lane = lane_id();
         asm volatile("" : "+v"(lane));
         const uint32_t col0 = part_elem0 + boff + lane * V;
         const uint32_t junk = s.junk + lane;
+        constexpr uint32_t kSign = D::kBytes == 4 ? 0x80000000u : 0x80008000u;
         uint32_t kmax = 0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const uint32_t kw = word_keys(r.v[u][w]);
+                const uint32_t kw = kPos ? (r.v[u][w] ^ kSign) : word_keys(r.v[u][w]);
                 const uint32_t wm = word_max(kw);
                 kmax = wm > kmax ? wm : kmax;
 #pragma unroll
                 for (int h = 0; h < V / 4; ++h) {
                     const int q = w * (V / 4) + h;
-                    const bool pred = (m >> (u * V + q)) & 1;
-                    if (__ballot(pred) != 0ull) {
-                        const uint32_t at = pred ? pos : junk;
-                        s.keys[at] = (typename D::Key)(h ? kw >> 16 : kw);
-                        s.idx[at] = col0 + (uint32_t)(u * UE + q);
-                        pos += pred ? 1u : 0u;
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
+                    const int b = u * V + q;
+                    const bool pred = (m >> b) & 1;
+                    uint32_t before;
+                    if constexpr (sizeof(MaskT) == 8)
+                        before = (uint32_t)__builtin_popcountll(m & ((1ull << b) - 1ull));
+                    else
+                        before = (uint32_t)__builtin_popcount((uint32_t)m & ((1u << b) - 1u));
+                    const uint32_t at = pred ? pos + before : junk;
+                    s.keys[at] = (typename D::Key)(h ? kw >> 16 : kw);
+                    s.idx[at] = col0 + (uint32_t)(u * UE + q);
                 }
             }
         }
@@ -738,9 +744,14 @@ struct RingStreamer {
             } else if (kMasks && c <= 64u) {
                 scatter_sparse(lm, incl - lc, lc, c, my_base, boff, slot, s.sparse + w * 64);
             } else if (kMasks) {
-                scatter_dense(r, lm, pos, boff);
+                if (th.neg)
+                    scatter_dense<false>(r, lm, pos, boff);
+                else
+                    scatter_dense<true>(r, lm, pos, boff);
+            } else if (th.neg) {
+                scatter_dense<false>(r, lane_bits<true>(r, th.thr), pos, boff);
             } else {
-                scatter_dense(r, th.neg ? lane_bits<true>(r, th.thr) : lane_bits<false>(r, th.thr), pos, boff);
+                scatter_dense<true>(r, lane_bits<false>(r, th.thr), pos, boff);
             }
         }
         st.A += run - st.len;
