@@ -1162,14 +1162,13 @@ struct MergeTile {
     uint32_t key[kMT], col[kMT];
 };
 
+// Tile t of part `part`'s results (lanes contiguous per load).
 template <int NW>
-__device__ __forceinline__ void load_merge_tile(MergeTile& t, const Params& p, const uint16_t* perm, int64_t row,
-                                                int64_t tile, uint32_t tiles_per_part) {
+__device__ __forceinline__ void load_part_tile(MergeTile& t, const Params& p, int64_t row, int64_t part,
+                                               uint32_t tile) {
     constexpr uint32_t TE = NW * 64 * kMT;
     const uint32_t k = (uint32_t)p.k;
-    const int64_t i = tile / tiles_per_part;
-    const uint32_t t0 = (uint32_t)(tile - i * tiles_per_part) * TE;
-    const int64_t part = (int64_t)uniform(perm[i]);
+    const uint32_t t0 = tile * TE;
     const int64_t off = (row * p.split + part) * (int64_t)k + t0;
 #pragma unroll
     for (int q = 0; q < kMT; ++q) {
@@ -1178,6 +1177,15 @@ __device__ __forceinline__ void load_merge_tile(MergeTile& t, const Params& p, c
         t.key[q] = inb ? p.ws_keys[off + e] : 0u;
         t.col[q] = inb ? p.ws_idx[off + e] : 0u;
     }
+}
+
+// Tile number `tile` of the merge: tile tile % tpp of the part at order
+// position tile / tpp.
+template <int NW>
+__device__ __forceinline__ void load_merge_tile(MergeTile& t, const Params& p, const uint16_t* perm, int64_t row,
+                                                int64_t tile, uint32_t tpp) {
+    const int64_t i = tile / tpp;
+    load_part_tile<NW>(t, p, row, (int64_t)uniform(perm[i]), (uint32_t)(tile - i * tpp));
 }
 
 template <class D, int NW>
@@ -1189,15 +1197,28 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
     const int32_t S = p.split;
     const uint32_t tpp = (k + TE - 1) / TE;  // tiles per part
     const int64_t tiles = (int64_t)S * tpp;
+    // with two tiles in all (two parts of one tile each: k <= NW*256), both
+    // are loaded before the order is built, which hides their latency
+    const bool both = tiles == 2 && tpp == 1;
     for (int64_t row = blockIdx.x; row < p.batch; row += gridDim.x) {
         __syncthreads();  // LDS free from the previous row
+        MergeTile cur, nxt, pre0, pre1;
+        if (both) {
+            load_part_tile<NW>(pre0, p, row, 0, 0);
+            load_part_tile<NW>(pre1, p, row, 1, 0);
+        }
         begin_item<D, NW>(s);
         build_order<NW>(s.perm, p.seed, row, 1, 0, S, s.base);
         RunState st;
-        MergeTile cur, nxt;
-        load_merge_tile<NW>(cur, p, s.perm, row, 0, tpp);
+        if (both) {
+            const bool swap = uniform(s.perm[0]) != 0u;
+            cur = swap ? pre1 : pre0;
+            nxt = swap ? pre0 : pre1;
+        } else {
+            load_merge_tile<NW>(cur, p, s.perm, row, 0, tpp);
+        }
         for (int64_t j = 0; j < tiles; ++j) {
-            if (j + 1 < tiles) load_merge_tile<NW>(nxt, p, s.perm, row, j + 1, tpp);
+            if (!both && j + 1 < tiles) load_merge_tile<NW>(nxt, p, s.perm, row, j + 1, tpp);
             const uint32_t t0 = (uint32_t)(j % tpp) * TE;
             const uint32_t tv = (k - t0) < TE ? (k - t0) : TE;
             uint32_t kmax = 0;
