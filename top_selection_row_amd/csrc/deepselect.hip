@@ -332,22 +332,23 @@ struct Streamer {
         }
         if (lane_id() == 0) s.cnt[st.par * NW + w] = c;
         __syncthreads();
-        uint32_t cs[NW];
-#pragma unroll
-        for (int g = 0; g < NW; ++g) cs[g] = uniform(s.cnt[st.par * NW + g]);
+        // the pages' order: block after block, compaction check after each.
+        // Lane g < NW takes block g's count (0 outside [first, nblk)); a
+        // prefix sum over those lanes gives the length after each block, the
+        // first lane reaching k + B2 is the trigger.
+        const int32_t lid = (int32_t)lane_id();
+        const bool inb = lid >= first && lid < nblk;
+        const uint32_t cg = inb ? s.cnt[st.par * NW + lid] : 0u;
         st.par ^= 1u;
-        // the pages' order: block after block, compaction check after each
-        uint32_t run = st.len, my_base = 0;
-        int32_t trig = -1;
-#pragma unroll
-        for (int g = 0; g < NW; ++g) {
-            if (g >= first && g < nblk && trig < 0) {
-                if (g == w) my_base = run;
-                run += cs[g];
-                if (run >= k + B2) trig = g;
-            }
-        }
+        uint32_t inc = cg;  // inclusive prefix over lanes 0..NW-1 (one DPP row)
+        inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x111, 0xF, 0xF, true);  // row_shr:1
+        inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x112, 0xF, 0xF, true);  // row_shr:2
+        inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x114, 0xF, 0xF, true);  // row_shr:4
+        const uint64_t over = __ballot(inb && st.len + inc >= k + B2);
+        const int32_t trig = over != 0ull ? (int32_t)__builtin_ctzll(over) : -1;
         const int32_t last = trig >= 0 ? trig : nblk - 1;
+        const uint32_t run = st.len + uniform(__builtin_amdgcn_readlane(inc, last));
+        const uint32_t my_base = st.len + uniform(__builtin_amdgcn_readlane(inc - cg, w));
         if (mine && w <= last && c != 0) {
             if (!st.tset)
                 scatter_all(r, my_base, boff, blen);
@@ -415,6 +416,7 @@ __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(15 | (3
 
 template <class D, int NW, int U>
 struct RingStreamer {
+    static_assert(NW <= 8, "the step's block counts are summed over one 8-lane DPP span");
     static constexpr int V = D::kPerLoad;
     static constexpr int UE = 64 * V;  // elements per unit
 
@@ -718,22 +720,23 @@ struct RingStreamer {
         const uint32_t c = uniform(__builtin_amdgcn_readlane(incl, 63));
         if (lane_id() == 0) s.cnt[st.par * NW + w] = c;
         __syncthreads();
-        uint32_t cs[NW];
-#pragma unroll
-        for (int g = 0; g < NW; ++g) cs[g] = uniform(s.cnt[st.par * NW + g]);
+        // the pages' order: block after block, compaction check after each.
+        // Lane g < NW takes block g's count (0 outside [first, nblk)); a
+        // prefix sum over those lanes gives the length after each block, the
+        // first lane reaching k + B2 is the trigger.
+        const int32_t lid = (int32_t)lane_id();
+        const bool inb = lid >= first && lid < nblk;
+        const uint32_t cg = inb ? s.cnt[st.par * NW + lid] : 0u;
         st.par ^= 1u;
-        // the pages' order: block after block, compaction check after each
-        uint32_t run = st.len, my_base = 0;
-        int32_t trig = -1;
-#pragma unroll
-        for (int g = 0; g < NW; ++g) {
-            if (g >= first && g < nblk && trig < 0) {
-                if (g == w) my_base = run;
-                run += cs[g];
-                if (run >= k + B2) trig = g;
-            }
-        }
+        uint32_t inc = cg;  // inclusive prefix over lanes 0..NW-1 (one DPP row)
+        inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x111, 0xF, 0xF, true);  // row_shr:1
+        inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x112, 0xF, 0xF, true);  // row_shr:2
+        inc += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)inc, 0x114, 0xF, 0xF, true);  // row_shr:4
+        const uint64_t over = __ballot(inb && st.len + inc >= k + B2);
+        const int32_t trig = over != 0ull ? (int32_t)__builtin_ctzll(over) : -1;
         const int32_t last = trig >= 0 ? trig : nblk - 1;
+        const uint32_t run = st.len + uniform(__builtin_amdgcn_readlane(inc, last));
+        const uint32_t my_base = st.len + uniform(__builtin_amdgcn_readlane(inc - cg, w));
         if (mine && w <= last && c != 0) {
             const uint32_t pos = my_base + incl - lc;
             if (!st.tset) {
