@@ -343,33 +343,19 @@ __device__ __forceinline__ uint32_t pick_bin(const uint32_t* folded, uint32_t& r
     const u32x4 c = reinterpret_cast<const u32x4*>(folded)[63 - lane];
     const uint32_t s = c.x + c.y + c.z + c.w;
     const uint32_t incl = wave_prefix_sum(s);
+    // every lane resolves its own 4 bins as if it held the rank-th key (vector
+    // selects, no branches); the lane that does is read back once
+    const uint32_t ex = incl - s;  // keys in the bins above this lane's
+    const uint32_t a3 = ex + c.w, a2 = a3 + c.z, a1 = a2 + c.y;
+    const bool h3 = a3 >= rank, h2 = a2 >= rank, h1 = a1 >= rank;
+    const uint32_t j = h3 ? 3u : h2 ? 2u : h1 ? 1u : 0u;
+    const uint32_t cnt = h3 ? c.w : h2 ? c.z : h1 ? c.y : c.x;
+    const uint32_t abv = h3 ? ex : h2 ? a3 : h1 ? a2 : a1;
     const uint64_t ge = __ballot(incl >= rank);
     const int L = __builtin_ctzll(ge);
-    const int g = 63 - L;
-    uint32_t above_cnt = uniform(__builtin_amdgcn_readlane(incl - s, L));
-    const uint32_t c3 = uniform(__builtin_amdgcn_readlane(c.w, L));
-    const uint32_t c2 = uniform(__builtin_amdgcn_readlane(c.z, L));
-    const uint32_t c1 = uniform(__builtin_amdgcn_readlane(c.y, L));
-    const uint32_t c0 = uniform(__builtin_amdgcn_readlane(c.x, L));
-    uint32_t d;
-    if (above_cnt + c3 >= rank) {
-        d = 4u * g + 3u;
-        count = c3;
-    } else if (above_cnt + c3 + c2 >= rank) {
-        above_cnt += c3;
-        d = 4u * g + 2u;
-        count = c2;
-    } else if (above_cnt + c3 + c2 + c1 >= rank) {
-        above_cnt += c3 + c2;
-        d = 4u * g + 1u;
-        count = c1;
-    } else {
-        above_cnt += c3 + c2 + c1;
-        d = 4u * g;
-        count = c0;
-    }
-    rank -= above_cnt;
-    return d;
+    count = uniform(__builtin_amdgcn_readlane(cnt, L));
+    rank -= uniform(__builtin_amdgcn_readlane(abv, L));
+    return 4u * (uint32_t)(63 - L) + uniform(__builtin_amdgcn_readlane(j, L));
 }
 
 // Stable in-place partition of keys/idx[0, n): keep every key > kth and the
