@@ -258,18 +258,24 @@ __device__ __forceinline__ void clear_words(uint32_t* p, uint32_t words) {
 // word). Lanes whose key is outside the window do not add; a chunk's keys are
 // checked against the end of the buffer only in the round that holds it, and
 // the next round's chunk is read before this one is counted.
-template <class D, int NW, bool kFull>
+template <class D, int NW, bool kFull, bool kAll>
 __device__ __forceinline__ void hist_chunk(const KeyChunk<D>& kc, uint32_t lim, uint32_t base, uint32_t span, int s,
                                            uint32_t* hl) {
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
         const uint32_t u = chunk_key<D>(kc, i) - base;
-        if ((kFull || (uint32_t)i < lim) && u <= span)
-            atomicAdd(&hl[((u >> (s + 1)) & 127u) * kHistCopies], 1u + ((u >> s) & 1u) * 0xFFFFu);
+        uint32_t* at = &hl[((u >> (s + 1)) & 127u) * kHistCopies];
+        const uint32_t inc = 1u + ((u >> s) & 1u) * 0xFFFFu;
+        if constexpr (kAll)
+            atomicAdd(at, (kFull || (uint32_t)i < lim) ? inc : 0u);
+        else if ((kFull || (uint32_t)i < lim) && u <= span)
+            atomicAdd(at, inc);
     }
 }
 
-template <class D, int NW>
+// kAll: every key of the buffer lies in the window (the first pass of a
+// select), so no lane skips its add.
+template <class D, int NW, bool kAll>
 __device__ __forceinline__ void hist_pass(const typename D::Key* keys, uint32_t n, uint32_t base, uint32_t span,
                                           int s, uint32_t* hist) {
     constexpr uint32_t NT = NW * 64;
@@ -283,9 +289,9 @@ __device__ __forceinline__ void hist_pass(const typename D::Key* keys, uint32_t 
         if (c0 + NT < nch) read_chunk<D>(nx, keys, c + NT < nch ? c + NT : 0u);  // the next round's chunk
         const uint32_t lim = c < nch ? n - c * kChunk : 0u;
         if (__ballot(lim < (uint32_t)kChunk) == 0ull)
-            hist_chunk<D, NW, true>(kc, lim, base, span, s, hl);
+            hist_chunk<D, NW, true, kAll>(kc, lim, base, span, s, hl);
         else
-            hist_chunk<D, NW, false>(kc, lim, base, span, s, hl);
+            hist_chunk<D, NW, false, kAll>(kc, lim, base, span, s, hl);
         kc = nx;
     }
 }
@@ -533,8 +539,13 @@ __device__ uint32_t select_topk(typename D::Key* keys, uint32_t* idx, uint32_t* 
     uint32_t base = lo, span = hi - lo, rank = k;
     int s = span ? 32 - __clz(span) : 0;  // bit length of the span
     s = s > 8 ? s - 8 : 0;
+    bool first = true;  // the first pass's window holds every key
     while (true) {
-        hist_pass<D, NW>(keys, n, base, span, s, hist);
+        if (first)
+            hist_pass<D, NW, true>(keys, n, base, span, s, hist);
+        else
+            hist_pass<D, NW, false>(keys, n, base, span, s, hist);
+        first = false;
         if (threadIdx.x == 0) *gcount = 0u;
         __syncthreads();
         fold_pass<NW>(hist, folded);
