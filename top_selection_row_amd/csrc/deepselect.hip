@@ -1204,20 +1204,26 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
     // are loaded before the order is built, which hides their latency
     const bool both = tiles == 2 && tpp == 1;
     for (int64_t row = blockIdx.x; row < p.batch; row += gridDim.x) {
-        __syncthreads();  // LDS free from the previous row
         MergeTile cur, nxt, pre0, pre1;
         if (both) {
             load_part_tile<NW>(pre0, p, row, 0, 0);
             load_part_tile<NW>(pre1, p, row, 1, 0);
         }
+        // the previous row's final select has ended, so the histogram and the
+        // largest-key cell are free to clear before the barrier that frees LDS
         begin_item<D, NW>(s);
-        build_order<NW>(s.perm, p.seed, row, 1, 0, S, s.base);
+        __syncthreads();
         RunState st;
         if (both) {
-            const bool swap = uniform(s.perm[0]) != 0u;
+            // two parts: the order is (part 1, part 0) exactly when part 1's
+            // hash is the smaller (ties go to the lower id), so every thread
+            // decides it from the two hashes, with no shared order
+            const uint64_t ctr0 = (uint64_t)(row * 2 + 1) << 32;
+            const bool swap = splitmix_at(p.seed, ctr0 + 1u) < splitmix_at(p.seed, ctr0);
             cur = swap ? pre1 : pre0;
             nxt = swap ? pre0 : pre1;
         } else {
+            build_order<NW>(s.perm, p.seed, row, 1, 0, S, s.base);
             load_merge_tile<NW>(cur, p, s.perm, row, 0, tpp);
         }
         for (int64_t j = 0; j < tiles; ++j) {
