@@ -820,13 +820,34 @@ template <class D, int NW>
 __device__ __forceinline__ void write_row(Lds<D>& s, const Params& p, int64_t row, uint64_t W, uint64_t A,
                                           uint64_t R, uint64_t maxlen) {
     const int64_t k = p.k;
-    for (int64_t j = threadIdx.x; j < k; j += NW * 64) {
-        const uint32_t key = s.keys[j];
-        if constexpr (D::kBytes == 4)
-            reinterpret_cast<uint32_t*>(p.out_vals)[row * k + j] = D::raw(key);
-        else
-            reinterpret_cast<uint16_t*>(p.out_vals)[row * k + j] = (uint16_t)D::raw(key);
-        p.out_idx[row * k + j] = (int32_t)s.idx[j];
+    // four entries per lane with 8- and 16-byte accesses when k and the
+    // output pointers allow it
+    const bool vec = (k % 4) == 0 && (reinterpret_cast<uintptr_t>(p.out_vals) % 16) == 0 &&
+                     (reinterpret_cast<uintptr_t>(p.out_idx) % 16) == 0;
+    if (vec) {
+        for (int64_t j = (int64_t)threadIdx.x * 4; j < k; j += NW * 64 * 4) {
+            const u32x4 iv = *reinterpret_cast<const u32x4*>(&s.idx[j]);
+            if constexpr (D::kBytes == 4) {
+                const u32x4 kv = *reinterpret_cast<const u32x4*>(&s.keys[j]);
+                *reinterpret_cast<u32x4*>(reinterpret_cast<uint32_t*>(p.out_vals) + row * k + j) =
+                    u32x4{D::raw(kv.x), D::raw(kv.y), D::raw(kv.z), D::raw(kv.w)};
+            } else {
+                const uint2 kv = *reinterpret_cast<const uint2*>(&s.keys[j]);
+                const uint32_t a = D::raw(kv.x & 0xFFFFu) | (D::raw(kv.x >> 16) << 16);
+                const uint32_t b = D::raw(kv.y & 0xFFFFu) | (D::raw(kv.y >> 16) << 16);
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out_vals) + row * k + j) = uint2{a, b};
+            }
+            *reinterpret_cast<u32x4*>(p.out_idx + row * k + j) = iv;
+        }
+    } else {
+        for (int64_t j = threadIdx.x; j < k; j += NW * 64) {
+            const uint32_t key = s.keys[j];
+            if constexpr (D::kBytes == 4)
+                reinterpret_cast<uint32_t*>(p.out_vals)[row * k + j] = D::raw(key);
+            else
+                reinterpret_cast<uint16_t*>(p.out_vals)[row * k + j] = (uint16_t)D::raw(key);
+            p.out_idx[row * k + j] = (int32_t)s.idx[j];
+        }
     }
     if (p.stats && threadIdx.x == 0) {
         uint64_t* o = p.stats + row * DS_STATS_PER_ROW;
@@ -840,9 +861,23 @@ __device__ __forceinline__ void write_row(Lds<D>& s, const Params& p, int64_t ro
 // Part results of split rows go to the workspace for the merge kernel.
 template <class D, int NW>
 __device__ __forceinline__ void write_part(Lds<D>& s, const RunState& st, const Params& p, int64_t slot) {
-    for (int64_t j = threadIdx.x; j < p.k; j += NW * 64) {
-        p.ws_keys[slot * p.k + j] = (uint32_t)s.keys[j];
-        p.ws_idx[slot * p.k + j] = s.idx[j];
+    if (p.k % 4 == 0) {  // the workspace arrays are 256-byte aligned
+        for (int64_t j = (int64_t)threadIdx.x * 4; j < p.k; j += NW * 64 * 4) {
+            u32x4 kv;
+            if constexpr (D::kBytes == 4) {
+                kv = *reinterpret_cast<const u32x4*>(&s.keys[j]);
+            } else {
+                const uint2 h = *reinterpret_cast<const uint2*>(&s.keys[j]);
+                kv = u32x4{h.x & 0xFFFFu, h.x >> 16, h.y & 0xFFFFu, h.y >> 16};
+            }
+            *reinterpret_cast<u32x4*>(p.ws_keys + slot * p.k + j) = kv;
+            *reinterpret_cast<u32x4*>(p.ws_idx + slot * p.k + j) = *reinterpret_cast<const u32x4*>(&s.idx[j]);
+        }
+    } else {
+        for (int64_t j = threadIdx.x; j < p.k; j += NW * 64) {
+            p.ws_keys[slot * p.k + j] = (uint32_t)s.keys[j];
+            p.ws_idx[slot * p.k + j] = s.idx[j];
+        }
     }
     if (threadIdx.x == 0) {
         uint64_t* o = p.ws_stats + slot * DS_STATS_PER_ROW;
