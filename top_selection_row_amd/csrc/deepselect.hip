@@ -187,6 +187,7 @@ __device__ __forceinline__ uint32_t test_word(const BlockRegs<U>& r, int u, int 
 // compaction code and lets the compaction run while later slots still load.
 template <class D, int NW, int U, int Q>
 struct Streamer {
+    static_assert(NW <= 8, "the step's block counts are summed over one 8-lane DPP span");
     static constexpr int V = D::kPerLoad;
     static constexpr int UE = 64 * V;  // elements per unit
 
