@@ -194,6 +194,18 @@ def test_edge_shapes(case):
     check_rows(x, vals, idx, k)
 
 
+@pytest.mark.parametrize("dt,k,split", [("bf16", 301, 3), ("f32", 77, 2), ("f32", 1, 5), ("bf16", 2, 4)])
+def test_split_odd_k(dt, k, split):
+    # k not a multiple of 4: the parts' results and the merged row are written
+    # one entry per lane (the four-at-a-time path needs k % 4 == 0)
+    batch, n, B, B2 = 6, 20000, 1024, 512
+    log(f"[gpu] split {split} with k {k}, {dt}")
+    x = synth.random_rows(batch, n, dt, 31, "gauss")
+    vals, idx, st = run_gpu(x, k, B, B2, seed=4, split=split)
+    check_rows(x, vals, idx, k)
+    check_stats_against_model(x, st, k, B, B2, 4, split, range(batch))
+
+
 def test_all_minus_inf_and_nan_rows():
     n, k = 5000, 300
     x = np.full((4, n), 0xFF80, dtype=np.uint16)  # all -inf
