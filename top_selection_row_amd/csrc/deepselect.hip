@@ -420,6 +420,19 @@ struct RingStreamer {
     static_assert(NW <= 8, "the step's block counts are summed over one 8-lane DPP span");
     static constexpr int V = D::kPerLoad;
     static constexpr int UE = 64 * V;  // elements per unit
+    static constexpr bool kPk = is_packed<D>::value;
+    static_assert(!kPk || V == 8, "packed entries are bfloat16 candidates");
+
+    // Store candidate (key, column col inside the part) at buffer position at:
+    // one packed entry, or the key and the row column in their two arrays.
+    __device__ __forceinline__ void put(uint32_t at, uint32_t key, uint32_t col) const {
+        if constexpr (kPk) {
+            s.keys[at] = (key << 16) | col;
+        } else {
+            s.keys[at] = (typename D::Key)key;
+            s.idx[at] = part_elem0 + col;
+        }
+    }
 
     Lds<D>& s;
     RunState& st;
@@ -551,7 +564,7 @@ struct RingStreamer {
                                                   uint32_t blen) const {
         uint32_t lane = lane_id();
         asm volatile("" : "+v"(lane));  // nothing here may be hoisted out of the retry loop
-        const uint32_t col0 = part_elem0 + boff + lane * V;
+        const uint32_t col0 = boff + lane * V;
         const uint32_t junk = s.junk + lane;
         uint32_t kmax = 0;
 #pragma unroll
@@ -561,8 +574,7 @@ struct RingStreamer {
                 const bool pred = u * UE + lane * V + q < blen;
                 const uint32_t key = D::key(raw_at<D, U>(r, u, q));
                 const uint32_t at = pred ? pos : junk;
-                s.keys[at] = (typename D::Key)key;
-                s.idx[at] = col0 + (uint32_t)(u * UE + q);
+                put(at, key, col0 + (uint32_t)(u * UE + q));
                 pos += pred ? 1u : 0u;
                 kmax = pred && key > kmax ? key : kmax;
                 __builtin_amdgcn_sched_barrier(0);
@@ -583,7 +595,7 @@ struct RingStreamer {
                                                   uint32_t boff) const {
         uint32_t lane = lane_id();
         asm volatile("" : "+v"(lane));
-        const uint32_t col0 = part_elem0 + boff + lane * V;
+        const uint32_t col0 = boff + lane * V;
         const uint32_t junk = s.junk + lane;
         constexpr uint32_t kSign = D::kBytes == 4 ? 0x80000000u : 0x80008000u;
         uint32_t kmax = 0;
@@ -605,8 +617,13 @@ struct RingStreamer {
                     else
                         before = (uint32_t)__builtin_popcount((uint32_t)m & ((1u << b) - 1u));
                     const uint32_t at = pred ? pos + before : junk;
-                    s.keys[at] = (typename D::Key)(h ? kw >> 16 : kw);
-                    s.idx[at] = col0 + (uint32_t)(u * UE + q);
+                    const uint32_t col = col0 + (uint32_t)(u * UE + q);
+                    if constexpr (kPk) {
+                        s.keys[at] = (h ? (kw & 0xFFFF0000u) : (kw << 16)) | col;
+                    } else {
+                        s.keys[at] = (typename D::Key)(h ? kw >> 16 : kw);
+                        s.idx[at] = part_elem0 + col;
+                    }
                 }
             }
         }
@@ -647,8 +664,7 @@ struct RingStreamer {
             const uint32_t raw = D::kBytes == 4 ? *reinterpret_cast<const uint32_t*>(p)
                                                 : (uint32_t)*reinterpret_cast<const uint16_t*>(p);
             key = D::key(raw);
-            s.keys[base + lane] = (typename D::Key)key;
-            s.idx[base + lane] = part_elem0 + boff + u * UE + src * V + q;
+            put(base + lane, key, boff + u * UE + src * V + q);
         }
         publish_max(s.misc, key);  // every lane takes part in the reduction
     }
@@ -661,7 +677,7 @@ struct RingStreamer {
         uint32_t lane = lane_id();
         asm volatile("" : "+v"(lane));  // nothing here may be hoisted out of the retry loop
         const uint32_t at0 = pos + lane * (U * V);
-        const uint32_t col0 = part_elem0 + boff + lane * V;
+        const uint32_t col0 = (kPk ? 0u : part_elem0) + boff + lane * V;
         uint32_t kmax = 0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -684,11 +700,22 @@ struct RingStreamer {
                 }
                 kw[q] = key;
             }
-            *reinterpret_cast<u32x4*>(&s.keys[at]) = kw;
             const uint32_t c = col0 + u * UE;
+            if constexpr (kPk) {
+                // entries key << 16 | column, two 16-byte stores per 8 elements
+                *reinterpret_cast<u32x4*>(&s.keys[at]) =
+                    u32x4{(kw[0] << 16) | c, (kw[0] & 0xFFFF0000u) | (c + 1), (kw[1] << 16) | (c + 2),
+                          (kw[1] & 0xFFFF0000u) | (c + 3)};
+                *reinterpret_cast<u32x4*>(&s.keys[at + 4]) =
+                    u32x4{(kw[2] << 16) | (c + 4), (kw[2] & 0xFFFF0000u) | (c + 5), (kw[3] << 16) | (c + 6),
+                          (kw[3] & 0xFFFF0000u) | (c + 7)};
+            } else {
+                *reinterpret_cast<u32x4*>(&s.keys[at]) = kw;
 #pragma unroll
-            for (int h = 0; h < V / 4; ++h)
-                *reinterpret_cast<u32x4*>(&s.idx[at + 4 * h]) = u32x4{c + 4 * h, c + 4 * h + 1, c + 4 * h + 2, c + 4 * h + 3};
+                for (int h = 0; h < V / 4; ++h)
+                    *reinterpret_cast<u32x4*>(&s.idx[at + 4 * h]) =
+                        u32x4{c + 4 * h, c + 4 * h + 1, c + 4 * h + 2, c + 4 * h + 3};
+            }
         }
         publish_max(s.misc, kmax);
     }
@@ -821,6 +848,14 @@ template <class D, int NW>
 __device__ __forceinline__ void write_row(Lds<D>& s, const Params& p, int64_t row, uint64_t W, uint64_t A,
                                           uint64_t R, uint64_t maxlen) {
     const int64_t k = p.k;
+    if constexpr (is_packed<D>::value) {
+        // one part per row: the entry's column is the row's
+        for (int64_t j = threadIdx.x; j < k; j += NW * 64) {
+            const uint32_t e = s.keys[j];
+            reinterpret_cast<uint16_t*>(p.out_vals)[row * k + j] = (uint16_t)D::raw(e >> 16);
+            p.out_idx[row * k + j] = (int32_t)(e & 0xFFFFu);
+        }
+    } else {
     // four entries per lane with 8- and 16-byte accesses when k and the
     // output pointers allow it
     const bool vec = (k % 4) == 0 && (reinterpret_cast<uintptr_t>(p.out_vals) % 16) == 0 &&
@@ -850,6 +885,7 @@ __device__ __forceinline__ void write_row(Lds<D>& s, const Params& p, int64_t ro
             p.out_idx[row * k + j] = (int32_t)s.idx[j];
         }
     }
+    }
     if (p.stats && threadIdx.x == 0) {
         uint64_t* o = p.stats + row * DS_STATS_PER_ROW;
         o[DS_STAT_W] = W;
@@ -861,8 +897,15 @@ __device__ __forceinline__ void write_row(Lds<D>& s, const Params& p, int64_t ro
 
 // Part results of split rows go to the workspace for the merge kernel.
 template <class D, int NW>
-__device__ __forceinline__ void write_part(Lds<D>& s, const RunState& st, const Params& p, int64_t slot) {
-    if (p.k % 4 == 0) {  // the workspace arrays are 256-byte aligned
+__device__ __forceinline__ void write_part(Lds<D>& s, const RunState& st, const Params& p, int64_t slot,
+                                           uint32_t part_elem0) {
+    if constexpr (is_packed<D>::value) {
+        for (int64_t j = threadIdx.x; j < p.k; j += NW * 64) {
+            const uint32_t e = s.keys[j];
+            p.ws_keys[slot * p.k + j] = e >> 16;
+            p.ws_idx[slot * p.k + j] = part_elem0 + (e & 0xFFFFu);
+        }
+    } else if (p.k % 4 == 0) {  // the workspace arrays are 256-byte aligned
         for (int64_t j = (int64_t)threadIdx.x * 4; j < p.k; j += NW * 64 * 4) {
             u32x4 kv;
             if constexpr (D::kBytes == 4) {
@@ -941,7 +984,7 @@ __global__ __launch_bounds__(NW * 64) void deepselect_stream_kernel(Params p) {
         if (p.split == 1)
             write_row<D, NW>(s, p, g.row, st.W, st.A, st.R, st.maxlen);
         else
-            write_part<D, NW>(s, st, p, g.slot);
+            write_part<D, NW>(s, st, p, g.slot, (uint32_t)g.part_elem0);
     }
 }
 
@@ -974,7 +1017,7 @@ __global__ __launch_bounds__(NW * 64) void deepselect_ring_kernel(Params p) {
         if (p.split == 1)
             write_row<D, NW>(s, p, g.row, st.W, st.A, st.R, st.maxlen);
         else
-            write_part<D, NW>(s, st, p, g.slot);
+            write_part<D, NW>(s, st, p, g.slot, (uint32_t)g.part_elem0);
     }
 }
 
@@ -1184,7 +1227,7 @@ __global__ __launch_bounds__(kGW * 64) void deepselect_generic_kernel(Params p) 
         if (p.split == 1)
             write_row<D, kGW>(s, p, g.row, st.W, st.A, st.R, st.maxlen);
         else
-            write_part<D, kGW>(s, st, p, g.slot);
+            write_part<D, kGW>(s, st, p, g.slot, (uint32_t)g.part_elem0);
     }
 }
 
@@ -1476,29 +1519,36 @@ static int launch_ring(int units, const Params& prm, size_t lds, hipStream_t st,
 // the generic kernel for rows the streaming kernels do not take.
 enum KernelKind { kAuto = 0, kRing = 1, kRegs = 2, kGeneric = 3 };
 
-template <class D>
+// D: the part kernel's candidate type (packed bfloat16 entries only in the
+// ring kernel); DM: the merge's, whose candidates carry row columns.
+template <class D, class DM>
 static int launch_all(KernelKind kind, int units, int waves, bool vec, Params prm, hipStream_t st, int64_t items) {
     int rc;
     const size_t lds = prm.L.total;
-    if (kind == kRing)
+    if constexpr (is_packed<D>::value) {
         rc = waves == 8 ? launch_ring<D, 8>(units, prm, lds, st, items) : launch_ring<D, 4>(units, prm, lds, st, items);
-    else if (kind == kRegs)
-        rc = waves == 8 ? launch_stream<D, 8>(units, prm, lds, st, items)
-                        : launch_stream<D, 4>(units, prm, lds, st, items);
-    else if (vec)
-        rc = launch_kernel(deepselect_generic_kernel<D, true>, items, kGW * 64, lds, st, prm);
-    else
-        rc = launch_kernel(deepselect_generic_kernel<D, false>, items, kGW * 64, lds, st, prm);
+    } else {
+        if (kind == kRing)
+            rc = waves == 8 ? launch_ring<D, 8>(units, prm, lds, st, items)
+                            : launch_ring<D, 4>(units, prm, lds, st, items);
+        else if (kind == kRegs)
+            rc = waves == 8 ? launch_stream<D, 8>(units, prm, lds, st, items)
+                            : launch_stream<D, 4>(units, prm, lds, st, items);
+        else if (vec)
+            rc = launch_kernel(deepselect_generic_kernel<D, true>, items, kGW * 64, lds, st, prm);
+        else
+            rc = launch_kernel(deepselect_generic_kernel<D, false>, items, kGW * 64, lds, st, prm);
+    }
     if (rc != DS_OK || prm.split == 1) return rc;
     // the merge runs on 8 waves when their layout fits, else on 4
-    const int dtype = D::kBytes == 4 ? DS_F32 : DS_BF16;
+    const int dtype = DM::kBytes == 4 ? DS_F32 : DS_BF16;
     const Layout M8 = make_merge_layout(dtype, prm.k, prm.B2, prm.split, 8);
     if (M8.total <= kLdsLimit) {
         prm.L = M8;
-        return launch_kernel(deepselect_merge_kernel<D, 8>, prm.batch, 8 * 64, prm.L.total, st, prm);
+        return launch_kernel(deepselect_merge_kernel<DM, 8>, prm.batch, 8 * 64, prm.L.total, st, prm);
     }
     prm.L = make_merge_layout(dtype, prm.k, prm.B2, prm.split, kGW);
-    return launch_kernel(deepselect_merge_kernel<D, kGW>, prm.batch, kGW * 64, prm.L.total, st, prm);
+    return launch_kernel(deepselect_merge_kernel<DM, kGW>, prm.batch, kGW * 64, prm.L.total, st, prm);
 }
 
 static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int32_t B,
@@ -1541,14 +1591,18 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     }
     Layout L = make_layout(dtype, n, k, B, B2, S, waves);
     if ((int64_t)L.total > (int64_t)di.lds) return DS_ERR_UNSUPPORTED;
+    bool packed = false;  // the ring kernel on packed bfloat16 entries
     if (kind != kGeneric) {
-        const Layout LR = with_ring(L, ceil_div(ceil_div(ceil_div(n, B), S), waves), units, (size_t)di.lds);
+        const bool pk = packed_parts(dtype, n, B, S);
+        const Layout LB = pk ? make_layout(dtype, n, k, B, B2, S, waves, true) : L;
+        const Layout LR = with_ring(LB, ceil_div(ceil_div(ceil_div(n, B), S), waves), units, (size_t)di.lds);
         if (req_kernel == kRing && LR.ring_depth == 0) return DS_ERR_UNSUPPORTED;
         if (req_kernel == kRegs || LR.ring_depth == 0) {
             kind = kRegs;
         } else {
             kind = kRing;
             L = LR;
+            packed = pk;
         }
     }
 
@@ -1584,8 +1638,9 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
         prm.ws_stats = reinterpret_cast<uint64_t*>(w + wl.stats);
     }
     const int64_t items = batch * S;
-    if (dtype == DS_F32) return launch_all<F32T>(kind, units, waves, vec, prm, hs, items);
-    return launch_all<BF16T>(kind, units, waves, vec, prm, hs, items);
+    if (dtype == DS_F32) return launch_all<F32T, F32T>(kind, units, waves, vec, prm, hs, items);
+    if (packed) return launch_all<BF16P, BF16T>(kind, units, waves, vec, prm, hs, items);
+    return launch_all<BF16T, BF16T>(kind, units, waves, vec, prm, hs, items);
 }
 
 }  // namespace ds

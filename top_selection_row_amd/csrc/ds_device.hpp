@@ -63,6 +63,27 @@ struct BF16T {
     __device__ static uint32_t raw(uint32_t key) { return raw_bf16(key); }
 };
 
+// bfloat16 candidates packed with their part-local column into one 32-bit
+// entry, key << 16 | column (parts of at most 65536 elements): one LDS store
+// per candidate instead of two. The select reads the key from the top half
+// and moves whole entries.
+struct BF16P {
+    using Key = uint32_t;
+    static constexpr int kBits = 16;
+    static constexpr int kBytes = 2;
+    static constexpr int kPerLoad = 8;
+    __device__ static uint32_t key(uint32_t raw) { return key_bf16(raw); }
+    __device__ static uint32_t raw(uint32_t key) { return raw_bf16(key); }
+};
+template <class D>
+struct is_packed {
+    static constexpr bool value = false;
+};
+template <>
+struct is_packed<BF16P> {
+    static constexpr bool value = true;
+};
+
 // Threshold test on raw bits, exact under the key order:
 //   T >= +0 : key(x) > key(T)  <=>  (int)x > (int)t
 //   T <  0  : key(x) > key(T)  <=>  (unsigned)x < (unsigned)t
@@ -228,19 +249,31 @@ constexpr uint32_t kHistWords = 128 * kHistCopies;  // 8 KiB
 
 template <class D>
 struct KeyChunk {
-    u32x4 v[D::kBytes == 4 ? 2 : 1];
+    u32x4 v[sizeof(typename D::Key) == 4 ? 2 : 1];
 };
 
 template <class D>
 __device__ __forceinline__ void read_chunk(KeyChunk<D>& kc, const typename D::Key* keys, uint32_t c) {
-    const u32x4* kv = reinterpret_cast<const u32x4*>(keys) + c * (D::kBytes == 4 ? 2u : 1u);
+    constexpr uint32_t W = sizeof(typename D::Key) == 4 ? 2u : 1u;
+    const u32x4* kv = reinterpret_cast<const u32x4*>(keys) + c * W;
     kc.v[0] = kv[0];
-    if constexpr (D::kBytes == 4) kc.v[1] = kv[1];
+    if constexpr (W == 2) kc.v[1] = kv[1];
 }
 
+// Key of entry i of a chunk, and the entry as stored (the same but for
+// packed entries, whose key is the top half).
 template <class D>
 __device__ __forceinline__ uint32_t chunk_key(const KeyChunk<D>& kc, int i) {
-    if constexpr (D::kBytes == 4)
+    if constexpr (is_packed<D>::value)
+        return kc.v[i >> 2][i & 3] >> 16;
+    else if constexpr (D::kBytes == 4)
+        return kc.v[i >> 2][i & 3];
+    else
+        return (kc.v[0][i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+}
+template <class D>
+__device__ __forceinline__ uint32_t chunk_entry(const KeyChunk<D>& kc, int i) {
+    if constexpr (sizeof(typename D::Key) == 4)
         return kc.v[i >> 2][i & 3];
     else
         return (kc.v[0][i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
@@ -395,9 +428,11 @@ __device__ __forceinline__ void partition_keep(typename D::Key* keys, uint32_t* 
                 const bool has = c < nch;
                 const uint32_t cr = has ? c : 0u;
                 read_chunk<D>(kc[r], keys, cr);
-                const u32x4* iv = reinterpret_cast<const u32x4*>(idx) + cr * 2u;
-                ix[r][0] = iv[0];
-                ix[r][1] = iv[1];
+                if constexpr (!is_packed<D>::value) {
+                    const u32x4* iv = reinterpret_cast<const u32x4*>(idx) + cr * 2u;
+                    ix[r][0] = iv[0];
+                    ix[r][1] = iv[1];
+                }
                 const uint32_t lim = has ? n - c * kChunk : 0u;
                 const uint32_t valid = lim >= (uint32_t)kChunk ? 0xFFu : ((1u << lim) - 1u);
                 uint32_t g = 0, e = 0;
@@ -452,8 +487,8 @@ __device__ __forceinline__ void partition_keep(typename D::Key* keys, uint32_t* 
                 for (int i = 0; i < kChunk; ++i) {
                     const bool kp = (km >> i) & 1u;
                     const uint32_t at = kp ? (uint32_t)__builtin_popcount(km & ((1u << i) - 1u)) + dst0 : my_junk;
-                    keys[at] = (typename D::Key)chunk_key<D>(kc[r], i);
-                    idx[at] = ix[r][i >> 2][i & 3];
+                    keys[at] = (typename D::Key)chunk_entry<D>(kc[r], i);
+                    if constexpr (!is_packed<D>::value) idx[at] = ix[r][i >> 2][i & 3];
                 }
                 run += all;
             }

@@ -78,15 +78,18 @@ struct Layout {
 inline int64_t capacity(int64_t k, int64_t blk, int64_t B2) { return k + blk + B2 - 1; }
 
 // order_n: ids in the random order (blocks of the largest part, or parts).
+// key_bytes 0: packed entries (a 16-bit key and a 16-bit part-local column in
+// one 32-bit word), with no column array.
 inline Layout make_layout_raw(int key_bytes, int64_t cap, int64_t order_n, int waves) {
     Layout L{};
     const int64_t capp = ceil_div(cap, kChunk) * kChunk;
     const int64_t entries = capp + 64;
+    const bool packed = key_bytes == 0;
     size_t off = 0;
     L.keys = 0;
-    off = align_up((size_t)entries * key_bytes, 16);
+    off = align_up((size_t)entries * (packed ? 4 : key_bytes), 16);
     L.idx = (uint32_t)off;
-    off = align_up(off + (size_t)entries * 4, 16);
+    if (!packed) off = align_up(off + (size_t)entries * 4, 16);
     // Building the block order uses the candidate arrays as scratch before the
     // scan starts: an 8-byte hash and a 4-byte rank or id per entry.
     off = std::max(off, align_up((size_t)next_pow2(std::max<int64_t>(order_n, 1)) * 12, 16));
@@ -114,9 +117,18 @@ inline Layout make_layout_raw(int key_bytes, int64_t cap, int64_t order_n, int w
 }
 
 // Layout of the streaming kernel: a part of ceil(m/S) blocks.
-inline Layout make_layout(int dtype, int64_t n, int64_t k, int64_t B, int64_t B2, int64_t S, int waves) {
+inline Layout make_layout(int dtype, int64_t n, int64_t k, int64_t B, int64_t B2, int64_t S, int waves,
+                          bool packed = false) {
     const int64_t m = ceil_div(n, B);
-    return make_layout_raw(elem_bytes(dtype), capacity(k, std::min<int64_t>(B, n), B2), ceil_div(m, S), waves);
+    return make_layout_raw(packed ? 0 : elem_bytes(dtype), capacity(k, std::min<int64_t>(B, n), B2), ceil_div(m, S),
+                           waves);
+}
+
+// bfloat16 parts of at most 65536 elements keep each candidate as one 32-bit
+// word, key << 16 | part-local column.
+inline bool packed_parts(int dtype, int64_t n, int64_t B, int64_t S) {
+    const int64_t m = ceil_div(n, B);
+    return dtype == 1 && ceil_div(m, S) * B <= 65536;
 }
 
 // Add a streaming ring to a layout: every wave gets `depth` slots of `units`
