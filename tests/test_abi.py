@@ -86,16 +86,16 @@ def test_split_plan_is_valid(name):
     L = w.k + w.block + w.block2 - 1
     assert L * (w.elem_bytes + 4) <= lds <= 160 * 1024
     # small batches are split towards one part per compute unit, within the
-    # planner's caps (balance of bytes to results, two 8-block steps per part,
+    # planner's caps (balance of bytes to results, four 8-block steps per part,
     # at most 16 parts)
     if w.batch <= 128:
-        cap = min(math.floor(math.sqrt(w.n * w.elem_bytes / (8 * w.k))), max(1, -(-w.n // w.block) // 16), 16)
+        cap = min(math.floor(math.sqrt(w.n * w.elem_bytes / (8 * w.k))), max(1, -(-w.n // w.block) // 32), 16)
         assert S == max(1, min(-(-256 // w.batch), cap))
 
 
 def test_split_plan_examples():
     assert ds.deepselect_plan_split(ds.DS_BF16, 128, 131072, 2048, 2048, 2048, 256) == 2
-    assert ds.deepselect_plan_split(ds.DS_F32, 64, 32768, 512, 1024, 1024, 256) == 2
+    assert ds.deepselect_plan_split(ds.DS_F32, 64, 32768, 512, 1024, 1024, 256) == 1
     assert ds.deepselect_plan_split(ds.DS_F32, 256, 151936, 64, 1024, 1024, 256) == 1
     assert ds.deepselect_plan_split(ds.DS_F32, 32, 1 << 20, 512, 1024, 1024, 256) == 8
     assert ds.deepselect_plan_split(ds.DS_F32, 1, 1 << 20, 512, 1024, 1024, 256) == 16

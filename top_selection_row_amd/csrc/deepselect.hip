@@ -1410,15 +1410,15 @@ static int plan_split(int dtype, int64_t batch, int64_t n, int32_t k, int32_t B,
     const int64_t lo = split_lower_bound(dtype, n, B);
     // Split when the rows fill at most half the compute units, about one
     // part per unit; no more parts than keep the streamed bytes of a part
-    // ahead of its k results (sqrt(N*size / 8k)), no part shorter than two
-    // steps of 8 blocks, and at most kSplitPlanMax parts (the merge grows
-    // with their number).
+    // ahead of its k results (sqrt(N*size / 8k)), no part shorter than four
+    // steps of 8 blocks (the merge's cost outweighs shorter parts), and at
+    // most kSplitPlanMax parts (the merge grows with their number).
     constexpr int64_t kSplitPlanMax = 16;
     int64_t S = 1;
     if (batch > 0 && batch <= num_cus / 2) S = ceil_div(num_cus, batch);
     const double bal = std::floor(std::sqrt((double)n * elem_bytes(dtype) / (8.0 * (double)k)));
     S = std::min<int64_t>(S, std::max<int64_t>(1, (int64_t)bal));
-    S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(n, B) / 16));
+    S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(n, B) / 32));
     S = std::min<int64_t>(S, kSplitPlanMax);
     S = std::max<int64_t>(S, lo);
     while (S > lo && (!split_ok(n, k, B, S) || !lds_fits(dtype, n, k, B, B2, S, kGW))) --S;
