@@ -297,8 +297,9 @@ __device__ __forceinline__ void hist_chunk(const KeyChunk<D>& kc, uint32_t lim, 
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
         const uint32_t u = chunk_key<D>(kc, i) - base;
-        uint32_t* at = &hl[((u >> (s + 1)) & 127u) * kHistCopies];
-        const uint32_t inc = 1u + ((u >> s) & 1u) * 0xFFFFu;
+        // bin pair (digit >> 1) and half (digit & 1) by bit-field extracts
+        uint32_t* at = &hl[__builtin_amdgcn_ubfe(u, (uint32_t)(s + 1), 7u) * kHistCopies];
+        const uint32_t inc = 1u + __builtin_amdgcn_ubfe(u, (uint32_t)s, 1u) * 0xFFFFu;
         if constexpr (kAll)
             atomicAdd(at, (kFull || (uint32_t)i < lim) ? inc : 0u);
         else if ((kFull || (uint32_t)i < lim) && u <= span)
