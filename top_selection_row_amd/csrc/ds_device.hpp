@@ -592,9 +592,11 @@ __device__ uint32_t select_topk(typename D::Key* keys, uint32_t* idx, uint32_t* 
         span = (1u << s) - 1u;
         // gathering pays off when two or more digits remain (32-bit keys);
         // for one more digit a plain pass is cheaper
-        if (cnt <= (uint32_t)kGather && s > 8) {
-            base = finish_gathered<D, NW>(keys, n, base, span, s, rank, hist, gathered, gcount);
-            break;
+        if constexpr (D::kBits > 16) {
+            if (cnt <= (uint32_t)kGather && s > 8) {
+                base = finish_gathered<D, NW>(keys, n, base, span, s, rank, hist, gathered, gcount);
+                break;
+            }
         }
         s = s > 8 ? s - 8 : 0;
     }
