@@ -68,6 +68,7 @@ struct RunState {
     uint64_t W = 0;     // RadixSelectTopK input (can pass 2^32 for huge k / tiny B2)
     uint32_t A = 0, R = 0, maxlen = 0;
     uint32_t par = 0;   // count-buffer parity
+    uint32_t kmax = 0;  // this wave's largest appended key
 };
 
 template <class D>
@@ -81,7 +82,7 @@ struct Lds {
     uint32_t* sparse;   // 64 words per wave (ring streaming: few-survivor scatter)
     uint32_t* cnt;
     uint16_t* perm;
-    uint32_t* misc;  // [1] largest key appended so far, [2] gathered-key counter
+    uint32_t* misc;  // [2] gathered-key counter, [8 + w] wave w's largest appended key
     unsigned char* base;
     uint32_t junk;   // first junk entry of the candidate arrays
 };
@@ -104,28 +105,37 @@ __device__ __forceinline__ Lds<D> lds_of(unsigned char* smem, const Layout& L) {
     return s;
 }
 
-// Start of a (row, part): clear the histogram copies and the largest-key cell
-// (the block order, built next, ends with a barrier).
+// Start of a (row, part): clear the histogram copies (the block order, built
+// next, ends with a barrier).
 template <class D, int NW>
 __device__ __forceinline__ void begin_item(Lds<D>& s) {
     clear_words<NW>(s.hist, kHistWords);
-    if (threadIdx.x == 0) s.misc[1] = 0u;
 }
 
-// Fold this wave's largest appended key into misc[1] (the top of the key range
-// the radix select starts from).
-__device__ __forceinline__ void publish_max(uint32_t* misc, uint32_t kmax) {
+// Fold the largest key this wave appended into its running maximum; the top
+// of the key range the radix select starts from is the largest over the
+// waves. A register, not an LDS atomic: the compiler makes every LDS atomic
+// wait for the wave's ring loads still in flight.
+__device__ __forceinline__ void publish_max(RunState& st, uint32_t kmax) {
     kmax = wave_max(kmax);
-    if (lane_id() == 0 && kmax != 0u) atomicMax(&misc[1], kmax);
+    st.kmax = kmax > st.kmax ? kmax : st.kmax;
 }
 
 // RadixSelectTopK(buffer, k): the buffer keeps its k largest and T becomes the
 // k-th key. Once T is set every candidate is >= T, the bottom of the key range.
 template <class D, int NW>
 __device__ __forceinline__ void select_buffer(Lds<D>& s, RunState& st, uint32_t k) {
+    static_assert(NW <= 8, "one largest-key cell per wave in misc[8..16)");
     const uint32_t lo = st.tset ? st.tkey : 0u;
-    __syncthreads();  // appends and the largest key are visible
-    const uint32_t hi = uniform(s.misc[1]);
+    if (lane_id() == 0) s.misc[8 + wave_id()] = st.kmax;
+    lds_barrier();  // appends and the waves' largest keys are visible
+    uint32_t hi = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const uint32_t v = s.misc[8 + i];
+        hi = v > hi ? v : hi;
+    }
+    hi = uniform(hi);
     st.tkey = select_topk<D, NW>(s.keys, s.idx, s.hist, s.fold, s.tot, s.gathered, s.misc + 2, s.junk, st.len, k, lo,
                                   hi > lo ? hi : lo);
     st.tset = true;
@@ -145,7 +155,7 @@ template <class D, int NW>
 __device__ __forceinline__ void final_select(Lds<D>& s, RunState& st, uint32_t k) {
     st.W += st.len;
     if (st.len > k) select_buffer<D, NW>(s, st, k);
-    __syncthreads();
+    lds_barrier();
 }
 
 // ===========================================================================
@@ -264,7 +274,7 @@ struct Streamer {
                 }
             }
         }
-        publish_max(s.misc, kmax);
+        publish_max(st, kmax);
     }
 
     // Append the elements of the block above T at base, in (unit, slot,
@@ -292,7 +302,7 @@ struct Streamer {
                 }
             }
         }
-        publish_max(s.misc, kmax);
+        publish_max(st, kmax);
     }
 
     // Copy slot j into the working block: a chain of uniform branches, one per
@@ -332,7 +342,7 @@ struct Streamer {
             }
         }
         if (lane_id() == 0) s.cnt[st.par * NW + w] = c;
-        __syncthreads();
+        lds_barrier();
         // the pages' order: block after block, compaction check after each.
         // Lane g < NW takes block g's count (0 outside [first, nblk)); a
         // prefix sum over those lanes gives the length after each block, the
@@ -580,7 +590,7 @@ struct RingStreamer {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        publish_max(s.misc, kmax);
+        publish_max(st, kmax);
     }
 
     // Append the lane's elements above T (mask m) at pos in element order:
@@ -627,7 +637,7 @@ struct RingStreamer {
                 }
             }
         }
-        publish_max(s.misc, kmax);
+        publish_max(st, kmax);
     }
 
     // Few survivors in the wave (c <= 64): survivor j is written by lane j.
@@ -666,7 +676,7 @@ struct RingStreamer {
             key = D::key(raw);
             put(base + lane, key, boff + u * UE + src * V + q);
         }
-        publish_max(s.misc, key);  // every lane takes part in the reduction
+        publish_max(st, key);  // every lane takes part in the reduction
     }
 
     // Append a whole full block at pos (before the first compaction, when
@@ -717,7 +727,7 @@ struct RingStreamer {
                         u32x4{c + 4 * h, c + 4 * h + 1, c + 4 * h + 2, c + 4 * h + 3};
             }
         }
-        publish_max(s.misc, kmax);
+        publish_max(st, kmax);
     }
 
     // Blocks first..nblk-1 of the step counted against the current state, then
@@ -747,7 +757,7 @@ struct RingStreamer {
         const uint32_t incl = wave_prefix_sum(lc);
         const uint32_t c = uniform(__builtin_amdgcn_readlane(incl, 63));
         if (lane_id() == 0) s.cnt[st.par * NW + w] = c;
-        __syncthreads();
+        lds_barrier();
         // the pages' order: block after block, compaction check after each.
         // Lane g < NW takes block g's count (0 outside [first, nblk)); a
         // prefix sum over those lanes gives the length after each block, the
@@ -965,7 +975,7 @@ __global__ __launch_bounds__(NW * 64) void deepselect_stream_kernel(Params p) {
     const int64_t items = p.batch * (int64_t)p.split;
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const PartGeom g = part_geom(p, item);
-        __syncthreads();  // LDS free from the previous item
+        lds_barrier();  // LDS free from the previous item
         begin_item<D, NW>(s);
         build_order<NW>(s.perm, p.seed, g.row, 0, g.b0, g.ms, s.base);
         RunState st;
@@ -996,7 +1006,7 @@ __global__ __launch_bounds__(NW * 64) void deepselect_ring_kernel(Params p) {
     const int64_t items = p.batch * (int64_t)p.split;
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const PartGeom g = part_geom(p, item);
-        __syncthreads();  // LDS free from the previous item
+        lds_barrier();  // LDS free from the previous item
         begin_item<D, NW>(s);
         build_order<NW>(s.perm, p.seed, g.row, 0, g.b0, g.ms, s.base);
         RunState st;
@@ -1040,7 +1050,7 @@ __device__ __forceinline__ uint32_t append_masked(const uint64_t (&masks)[NS], c
     for (int q = 0; q < NS; ++q) c += (uint32_t)__popcll(masks[q]);
     const int wave = wave_id();
     if (lane_id() == 0) cnt[par * NW + wave] = c;
-    __syncthreads();
+    lds_barrier();
     uint32_t base = 0, total = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -1135,7 +1145,7 @@ __device__ __forceinline__ void generic_tile(Lds<D>& s, RunState& st, const Tile
                 kmax = key > kmax ? key : kmax;
             }
         }
-        publish_max(s.misc, kmax);
+        publish_max(st, kmax);
         st.len += (uint32_t)tv;
         st.A += (uint32_t)tv;
         return;
@@ -1154,7 +1164,7 @@ __device__ __forceinline__ void generic_tile(Lds<D>& s, RunState& st, const Tile
         s.idx[pos] = (uint32_t)(col0 + tile_elem<D, kVec>(q));
         kmax = key > kmax ? key : kmax;
     });
-    publish_max(s.misc, kmax);
+    publish_max(st, kmax);
     st.len += added;
     st.A += added;
 }
@@ -1218,7 +1228,7 @@ __global__ __launch_bounds__(kGW * 64) void deepselect_generic_kernel(Params p) 
     const int64_t items = p.batch * (int64_t)p.split;
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const PartGeom g = part_geom(p, item);
-        __syncthreads();
+        lds_barrier();
         begin_item<D, kGW>(s);
         build_order<kGW>(s.perm, p.seed, g.row, 0, g.b0, g.ms, s.base);
         RunState st;
@@ -1291,7 +1301,7 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
         // the previous row's final select has ended, so the histogram and the
         // largest-key cell are free to clear before the barrier that frees LDS
         begin_item<D, NW>(s);
-        __syncthreads();
+        lds_barrier();
         RunState st;
         if (both) {
             // two parts: the order is (part 1, part 0) exactly when part 1's
@@ -1340,7 +1350,7 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
                 st.len += added;
                 st.A += added;
             }
-            publish_max(s.misc, kmax);
+            publish_max(st, kmax);
             if ((j + 1) % tpp == 0) {  // a part's block ends: the compaction check
                 st.maxlen = st.len > st.maxlen ? st.len : st.maxlen;
                 if (st.len >= k + B2) compact<D, NW>(s, st, k);

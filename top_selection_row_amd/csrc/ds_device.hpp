@@ -24,6 +24,13 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Workgroup barrier for LDS traffic: waits for this wave's LDS operations
+// only. __syncthreads() also waits for every outstanding vector-memory
+// operation, which would stall each step on the ring's prefetches into LDS;
+// no kernel here exchanges global memory between its waves, and each wave
+// waits (vmcnt) for its own ring blocks before it reads them.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Number of set bits of m in the lanes below this one.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -148,7 +155,7 @@ __device__ void build_order(uint16_t* perm, uint64_t seed, int64_t row, int tag,
             hk[t] = splitmix_at(seed, ctr0 + (uint64_t)t);
             rank[t] = 0u;
         }
-        __syncthreads();
+        lds_barrier();
         const int lo = wave * count / NW, hi = (wave + 1) * count / NW;
         for (int j = lane; j < count; j += 64) {
             const uint64_t h = hk[j];
@@ -159,7 +166,7 @@ __device__ void build_order(uint16_t* perm, uint64_t seed, int64_t row, int tag,
             }
             if (r) atomicAdd(&rank[j], r);
         }
-        __syncthreads();
+        lds_barrier();
         if (t < count) perm[rank[t]] = (uint16_t)t;
     } else {
         const int p2 = (int)next_pow2(count);
@@ -168,7 +175,7 @@ __device__ void build_order(uint16_t* perm, uint64_t seed, int64_t row, int tag,
             hk[i] = i < count ? splitmix_at(seed, ctr0 + (uint64_t)i) : ~0ull;
             hid[i] = (uint32_t)i;
         }
-        __syncthreads();
+        lds_barrier();
         for (int size = 2; size <= p2; size <<= 1) {
             for (int stride = size >> 1; stride > 0; stride >>= 1) {
                 for (int i = t; i < p2; i += kLanes) {
@@ -185,12 +192,12 @@ __device__ void build_order(uint16_t* perm, uint64_t seed, int64_t row, int tag,
                         }
                     }
                 }
-                __syncthreads();
+                lds_barrier();
             }
         }
         for (int i = t; i < count; i += kLanes) perm[i] = (uint16_t)hid[i];
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // Largest value over the wave, returned uniform (a DPP max scan whose last
@@ -450,7 +457,7 @@ __device__ __forceinline__ void partition_keep(typename D::Key* keys, uint32_t* 
                 if (lane == 63) tot[(par * R + r) * NW + wave] = incl[r];
             }
         }
-        __syncthreads();
+        lds_barrier();
         const u32x4* tv = reinterpret_cast<const u32x4*>(tot + par * R * NW);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -538,7 +545,7 @@ __device__ __forceinline__ uint32_t finish_gathered(const typename D::Key* keys,
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     const uint32_t ng = min(uniform(*gcount), (uint32_t)kGather);
     const int lane = lane_id();
     uint32_t g[kGather / 64];
@@ -571,7 +578,7 @@ template <class D, int NW>
 __device__ uint32_t select_topk(typename D::Key* keys, uint32_t* idx, uint32_t* hist, uint32_t* folded,
                                 uint32_t* tot, uint32_t* gathered, uint32_t* gcount, uint32_t junk, uint32_t n,
                                 uint32_t k, uint32_t lo, uint32_t hi) {
-    __syncthreads();
+    lds_barrier();
     uint32_t base = lo, span = hi - lo, rank = k;
     int s = span ? 32 - __clz(span) : 0;  // bit length of the span
     s = s > 8 ? s - 8 : 0;
@@ -583,9 +590,9 @@ __device__ uint32_t select_topk(typename D::Key* keys, uint32_t* idx, uint32_t* 
             hist_pass<D, NW, false>(keys, n, base, span, s, hist);
         first = false;
         if (threadIdx.x == 0) *gcount = 0u;
-        __syncthreads();
+        lds_barrier();
         fold_pass<NW>(hist, folded);
-        __syncthreads();
+        lds_barrier();
         uint32_t cnt;
         base += pick_bin(folded, rank, cnt) << s;
         if (s == 0) break;
