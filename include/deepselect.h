@@ -97,6 +97,13 @@ typedef struct ds_options {
      * streaming kernels take (see `waves`); others run the generic kernel.
      * Any other value: DS_ERR_BLOCK. */
     int32_t kernel;
+    /* Order of each output row: 0 = no particular order; 1 = descending, equal
+     * values by ascending column (the worked example of "CUDA 算子笔记 4",
+     * section "Top K Selection", lists its result largest first). The results
+     * are sorted in LDS before they are written: next_pow2(k) * 8 more bytes of
+     * LDS, so a shape near the limit may give DS_ERR_UNSUPPORTED. The result
+     * set is the same either way. Any other value: DS_ERR_BLOCK. */
+    int32_t sorted;
 } ds_options_t;
 
 /* Check arguments only (pure host code, no HIP call; usable without a GPU).
@@ -109,7 +116,8 @@ int deepselect_topk(const void *x, int dtype, int64_t batch, int64_t N, int64_t 
                     int32_t k, int32_t B, int32_t B2, uint64_t seed, void *out_vals,
                     int32_t *out_idx, void *stream);
 
-/* deepselect_topk with options (forced split, statistics, caller workspace).
+/* deepselect_topk with options (forced split, statistics, caller workspace,
+ * sorted output).
  * opt may be NULL (then identical to deepselect_topk). */
 int deepselect_topk_ex(const void *x, int dtype, int64_t batch, int64_t N, int64_t row_stride,
                        int32_t k, int32_t B, int32_t B2, uint64_t seed, void *out_vals,

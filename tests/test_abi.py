@@ -56,6 +56,37 @@ def test_topk_rejects_before_any_hip_call():
     assert ds.deepselect_topk(18, ds.DS_F32, 2, 64, 64, 8, 16, 16, 0, 16, 16, 0) == ds.DS_ERR_SHAPE
 
 
+def test_topk_ex_rejects_bad_options_before_any_hip_call():
+    # the options are checked with the other arguments, before the device is
+    # queried (none exists here, so reaching it would give DS_ERR_HIP)
+    args = (16, ds.DS_F32, 2, 64, 64, 8, 16, 16, 0, 16, 16, 0)
+    assert ds.deepselect_topk_ex(*args, waves=5) == ds.DS_ERR_BLOCK
+    assert ds.deepselect_topk_ex(*args, kernel=4) == ds.DS_ERR_BLOCK
+    assert ds.deepselect_topk_ex(*args, kernel=-1) == ds.DS_ERR_BLOCK
+    assert ds.deepselect_topk_ex(*args, sorted=2) == ds.DS_ERR_BLOCK
+    assert ds.deepselect_topk_ex(*args, sorted=-1) == ds.DS_ERR_BLOCK
+
+
+def test_options_struct_matches_the_header(tmp_path):
+    # the binding's ds_options_t against the C compiler's reading of the header
+    import ctypes
+    import pathlib
+    import subprocess
+    names = [f[0] for f in ds.DsOptions._fields_]
+    inc = pathlib.Path(__file__).resolve().parents[1] / "include"
+    src = tmp_path / "opt.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"deepselect.h\"\n"
+                   "int main(void) { printf(\"%zu\", sizeof(ds_options_t));"
+                   + "".join(f' printf(" %zu", offsetof(ds_options_t, {n}));' for n in names)
+                   + " return 0; }\n")
+    exe = tmp_path / "opt"
+    subprocess.run(["gcc", "-I", str(inc), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(ds.DsOptions)
+    assert got[1:] == [getattr(ds.DsOptions, n).offset for n in names]
+
+
 def test_status_strings():
     for st in range(0, -9, -1):
         s = ds.deepselect_status_string(st)

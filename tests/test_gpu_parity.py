@@ -50,9 +50,9 @@ def raw_of(t):
     raise TypeError(t.dtype)
 
 
-def run_gpu(x: np.ndarray, k, B, B2, seed=0, split=0, stats=True, waves=0, kernel=0):
+def run_gpu(x: np.ndarray, k, B, B2, seed=0, split=0, stats=True, waves=0, kernel=0, sorted=False):
     xt = to_device(x)
-    out = ds.topk(xt, k, B, B2, seed, split=split, stats=stats, waves=waves, kernel=kernel)
+    out = ds.topk(xt, k, B, B2, seed, split=split, stats=stats, waves=waves, kernel=kernel, sorted=sorted)
     torch.cuda.synchronize()
     vals, idx = raw_of(out[0]), out[1].cpu().numpy()
     st = out[2].cpu().numpy() if stats else None
@@ -76,6 +76,32 @@ def check_rows(x: np.ndarray, vals, idx, k, rows=None):
         kth = want[0]
         if k == n or int((keys_r >= kth).sum()) == k:
             assert np.array_equal(np.sort(idx[r]), np.sort(o_idx[r])), f"row {r}: index set differs"
+
+
+def check_sorted_rows(x: np.ndarray, vals, idx, k, rows=None):
+    """Sorted output: the oracle's (key desc, column asc) order, exactly.
+
+    Keys match the oracle position by position; equal keys come by ascending
+    column; every entry above the k-th key is the oracle's own; when no tie
+    crosses the cut the whole index array is the oracle's.
+    """
+    raw, _ = oracle.raw_bits(x)
+    o_vals, o_idx = oracle.topk(x, k)
+    n = x.shape[1]
+    rows = range(x.shape[0]) if rows is None else rows
+    for r in rows:
+        assert len(np.unique(idx[r])) == k, f"row {r}: repeated index"
+        assert idx[r].min() >= 0 and idx[r].max() < n, f"row {r}: index out of range"
+        assert np.array_equal(raw[r][idx[r]], vals[r]), f"row {r}: value bits differ from x[idx]"
+        got, want = oracle.keys(vals[r]), oracle.keys(o_vals[r])
+        assert np.array_equal(got, want), f"row {r}: keys not in the oracle's order"
+        same = got[1:] == got[:-1]
+        assert np.all(idx[r][1:][same] > idx[r][:-1][same]), f"row {r}: equal keys not by ascending column"
+        kth = want[-1]
+        above = got > kth
+        assert np.array_equal(idx[r][above], o_idx[r][above]), f"row {r}: entries above the k-th differ"
+        if int((oracle.keys(raw[r]) >= kth).sum()) == k:
+            assert np.array_equal(idx[r], o_idx[r]), f"row {r}: index order differs"
 
 
 def check_stats_against_model(x, st, k, B, B2, seed, split, rows):
@@ -288,3 +314,38 @@ def test_library_workspace_across_shapes():
         vals, idx, st = run_gpu(x[:batch], w.k, w.block, w.block2, split=S)
         check_rows(x[:batch], vals, idx, w.k)
         check_stats_against_model(x[:batch], st, w.k, w.block, w.block2, 0, S, range(2))
+
+
+# ---------------------------------------------------------------- sorted output
+
+SORTED = [
+    # (workload, rows, split, waves, kernel, k or None for the workload's)
+    ("dsa128k_bf16", 6, 1, 8, 1, None),   # ring streaming, packed bfloat16 candidates
+    ("dsa128k_bf16", 6, 2, 8, 0, None),   # split rows: the merge kernel sorts
+    ("dsa32k", 8, 1, 8, 1, None),         # ring streaming, float32
+    ("dsa32k", 8, 1, 4, 2, None),         # register streaming
+    ("vocab152k_k64", 8, 0, 0, 3, None),  # generic kernel
+    ("ties1m", 2, 0, 0, 0, None),         # every result ties: columns ascending
+    ("asc1m_b1", 1, 0, 0, 0, None),       # one row in many parts
+    ("gauss4k", 1, 1, 8, 0, 1),
+    ("gauss4k", 1, 1, 8, 0, 3),
+    ("gauss4k", 1, 1, 8, 0, 300),         # k not a power of two
+    ("gauss4k", 1, 1, 4, 0, 4096),        # k = N
+]
+
+
+@pytest.mark.parametrize("case", SORTED, ids=[f"{c[0]}-S{c[2]}-w{c[3]}-kern{c[4]}-k{c[5]}" for c in SORTED])
+def test_sorted_output(case):
+    name, rows, split, waves, kernel, k = case
+    w = synth.WORKLOADS[name]
+    k = w.k if k is None else k
+    log(f"[gpu] sorted output {case}")
+    x = synth.generate(name, rows)
+    vals, idx, st = run_gpu(x, k, w.block, w.block2, seed=3, split=split, waves=waves, kernel=kernel,
+                            sorted=True)
+    check_sorted_rows(x, vals, idx, k)
+    # the same set and the same control flow as the unsorted call
+    u_vals, u_idx, u_st = run_gpu(x, k, w.block, w.block2, seed=3, split=split, waves=waves, kernel=kernel)
+    assert np.array_equal(st, u_st)
+    for r in range(rows):
+        assert np.array_equal(np.sort(idx[r]), np.sort(u_idx[r]))

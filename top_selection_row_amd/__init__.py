@@ -34,7 +34,8 @@ EXPORTS = (
 class DsOptions(ctypes.Structure):
     _fields_ = [("split", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("stats", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("kernel", ctypes.c_int32)]
+                ("workspace_bytes", ctypes.c_size_t), ("kernel", ctypes.c_int32),
+                ("sorted", ctypes.c_int32)]
 
 
 _lib = None
@@ -120,8 +121,9 @@ def deepselect_topk(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals, ou
 
 
 def deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals, out_idx, stream,
-                       split=0, stats=None, workspace=None, workspace_bytes=0, waves=0, kernel=0) -> int:
-    opt = DsOptions(int(split), int(waves), stats, workspace, int(workspace_bytes), int(kernel))
+                       split=0, stats=None, workspace=None, workspace_bytes=0, waves=0, kernel=0,
+                       sorted=0) -> int:
+    opt = DsOptions(int(split), int(waves), stats, workspace, int(workspace_bytes), int(kernel), int(sorted))
     return library().deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed & (2**64 - 1),
                                         out_vals, out_idx, stream, ctypes.byref(opt))
 
@@ -129,7 +131,7 @@ def deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals,
 # ---------------------------------------------------------------- torch wrapper
 
 def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, waves: int = 0,
-         kernel: int = 0, stats: bool = False, out=None, stream=None):
+         kernel: int = 0, stats: bool = False, sorted: bool = False, out=None, stream=None):
     """Row-wise top-k of a 2-D CUDA tensor (float32 or bfloat16, unit column stride).
 
     ``kernel``: 0 library choice, 1 ring streaming, 2 register streaming,
@@ -137,7 +139,8 @@ def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, waves: in
 
     Returns (vals [batch, k] same dtype, idx [batch, k] int32) and, with
     ``stats=True``, a [batch, 4] int64 tensor (W, A, R, max_len). The k entries
-    of a row are in no particular order. Raises on any rejected argument.
+    of a row are in no particular order, or with ``sorted=True`` largest first
+    (equal values by ascending column). Raises on any rejected argument.
     """
     import torch
 
@@ -164,7 +167,8 @@ def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, waves: in
     with torch.cuda.device(x.device):
         _check(deepselect_topk_ex(x.data_ptr(), dt, batch, n, row_stride, k, B, B2, seed,
                                   vals.data_ptr(), idx.data_ptr(), stream, split=split, waves=waves,
-                                  kernel=kernel, stats=st.data_ptr() if st is not None else None))
+                                  kernel=kernel, stats=st.data_ptr() if st is not None else None,
+                                  sorted=int(bool(sorted))))
     if stats:
         return vals, idx, st
     return vals, idx

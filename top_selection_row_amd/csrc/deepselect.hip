@@ -58,6 +58,7 @@ struct Params {
     int64_t batch, n, row_stride, m;
     uint64_t seed;
     int32_t k, B, B2, split;
+    int32_t sorted;  // write each row's results in descending order
     Layout L;
 };
 
@@ -854,11 +855,84 @@ struct RingStreamer {
 template <class D, int NW, int U>
 __global__ __launch_bounds__(NW * 64) void deepselect_ring_kernel(Params p);
 
+// Descending bitonic sort of the n2 (a power of two) 64-bit words at a: the
+// network of Batcher that "CUDA 算子笔记 4" ("Top K Selection", the bitonic
+// approach) sorts its candidates with. In the stage of distance j, pair q
+// (thread q mod NT) joins word i = q with a zero bit inserted at log2(j) and
+// word i + j. While j < 64 the 64 pairs a wave takes at once stay inside the
+// same 128 words whatever j is, so consecutive such stages need only the
+// wave's own (in-order) LDS accesses; every other stage waits for the
+// workgroup. Starts and ends with a workgroup barrier.
+template <int NW>
+__device__ __forceinline__ void bitonic_desc(uint64_t* a, uint32_t n2) {
+    constexpr uint32_t NT = NW * 64;
+    const uint32_t half = n2 >> 1;
+    bool local = false;  // the previous stage kept to each wave's words
+    for (uint32_t size = 2; size <= n2; size <<= 1) {
+        for (uint32_t j = size >> 1; j > 0; j >>= 1) {
+            const bool here = j < 64;
+            if (here && local)
+                asm volatile("" ::: "memory");  // keep the compiler from reordering across stages
+            else
+                lds_barrier();
+            local = here;
+            for (uint32_t q = threadIdx.x; q < half; q += NT) {
+                const uint32_t i = ((q & ~(j - 1)) << 1) | (q & (j - 1));
+                const uint64_t x = a[i], y = a[i + j];
+                if ((i & size) == 0 ? x < y : x > y) {
+                    a[i] = y;
+                    a[i + j] = x;
+                }
+            }
+        }
+    }
+    lds_barrier();
+}
+
+// The row's k results as sort words key << 32 | ~column, descending: keys
+// from the largest down, equal keys by ascending column. Padding words are 0,
+// below every result (~column >= 2^31).
+template <class D, int NW>
+__device__ __forceinline__ const uint64_t* sort_results(Lds<D>& s, const Params& p) {
+    uint64_t* a = reinterpret_cast<uint64_t*>(s.base + p.L.sort);
+    const uint32_t k = (uint32_t)p.k;
+    const uint32_t n2 = k <= 1u ? 1u : 1u << (32 - __clz(k - 1u));
+    for (uint32_t j = threadIdx.x; j < n2; j += NW * 64) {
+        uint64_t w = 0;
+        if (j < k) {
+            uint32_t key, col;
+            if constexpr (is_packed<D>::value) {
+                const uint32_t e = s.keys[j];
+                key = e >> 16;
+                col = e & 0xFFFFu;
+            } else {
+                key = s.keys[j];
+                col = s.idx[j];
+            }
+            w = ((uint64_t)key << 32) | (uint32_t)~col;
+        }
+        a[j] = w;
+    }
+    bitonic_desc<NW>(a, n2);
+    return a;
+}
+
 template <class D, int NW>
 __device__ __forceinline__ void write_row(Lds<D>& s, const Params& p, int64_t row, uint64_t W, uint64_t A,
                                           uint64_t R, uint64_t maxlen) {
     const int64_t k = p.k;
-    if constexpr (is_packed<D>::value) {
+    if (p.sorted) {
+        const uint64_t* a = sort_results<D, NW>(s, p);
+        for (int64_t j = threadIdx.x; j < k; j += NW * 64) {
+            const uint64_t w = a[j];
+            const uint32_t key = (uint32_t)(w >> 32);
+            if constexpr (D::kBytes == 4)
+                reinterpret_cast<uint32_t*>(p.out_vals)[row * k + j] = D::raw(key);
+            else
+                reinterpret_cast<uint16_t*>(p.out_vals)[row * k + j] = (uint16_t)D::raw(key);
+            p.out_idx[row * k + j] = (int32_t)~(uint32_t)w;
+        }
+    } else if constexpr (is_packed<D>::value) {
         // one part per row: the entry's column is the row's
         for (int64_t j = threadIdx.x; j < k; j += NW * 64) {
             const uint32_t e = s.keys[j];
@@ -1409,10 +1483,17 @@ static int stream_units(int dtype, int64_t B) {
     return 0;
 }
 
-static bool lds_fits(int dtype, int64_t n, int64_t k, int64_t B, int64_t B2, int64_t S, int waves) {
+static bool lds_fits(int dtype, int64_t n, int64_t k, int64_t B, int64_t B2, int64_t S, int waves,
+                     bool sorted = false) {
     if (k + std::min<int64_t>(B, n) + B2 > ((int64_t)1 << 30)) return false;
-    if (make_layout(dtype, n, k, B, B2, S, waves).total > kLdsLimit) return false;
-    if (S > 1 && make_merge_layout(dtype, k, B2, S, kGW).total > kLdsLimit) return false;
+    Layout L = make_layout(dtype, n, k, B, B2, S, waves);
+    if (sorted && S == 1) L = with_sort(L, k);
+    if (L.total > kLdsLimit) return false;
+    if (S > 1) {
+        Layout M = make_merge_layout(dtype, k, B2, S, kGW);
+        if (sorted) M = with_sort(M, k);
+        if (M.total > kLdsLimit) return false;
+    }
     return true;
 }
 
@@ -1552,12 +1633,14 @@ static int launch_all(KernelKind kind, int units, int waves, bool vec, Params pr
     if (rc != DS_OK || prm.split == 1) return rc;
     // the merge runs on 8 waves when their layout fits, else on 4
     const int dtype = DM::kBytes == 4 ? DS_F32 : DS_BF16;
-    const Layout M8 = make_merge_layout(dtype, prm.k, prm.B2, prm.split, 8);
+    Layout M8 = make_merge_layout(dtype, prm.k, prm.B2, prm.split, 8);
+    if (prm.sorted) M8 = with_sort(M8, prm.k);
     if (M8.total <= kLdsLimit) {
         prm.L = M8;
         return launch_kernel(deepselect_merge_kernel<DM, 8>, prm.batch, 8 * 64, prm.L.total, st, prm);
     }
     prm.L = make_merge_layout(dtype, prm.k, prm.B2, prm.split, kGW);
+    if (prm.sorted) prm.L = with_sort(prm.L, prm.k);
     return launch_kernel(deepselect_merge_kernel<DM, kGW>, prm.batch, kGW * 64, prm.L.total, st, prm);
 }
 
@@ -1572,6 +1655,10 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     if (((uintptr_t)x % es) != 0) return DS_ERR_SHAPE;
     const int req_waves = opt ? opt->waves : 0;
     if (req_waves != 0 && req_waves != 4 && req_waves != 8) return DS_ERR_BLOCK;
+    const int req_kernel = opt ? opt->kernel : 0;
+    if (req_kernel < kAuto || req_kernel > kGeneric) return DS_ERR_BLOCK;
+    const int sorted = opt ? opt->sorted : 0;
+    if (sorted != 0 && sorted != 1) return DS_ERR_BLOCK;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DS_ERR_HIP;
     DevInfo di;
@@ -1588,23 +1675,28 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     const bool vec = ((uintptr_t)x % 16 == 0) && ((row_stride * es) % 16 == 0) && (((int64_t)B * es) % 16 == 0) &&
                      ((n * es) % 16 == 0);
     const int units = vec ? stream_units(dtype, B) : 0;
-    const int req_kernel = opt ? opt->kernel : 0;
-    if (req_kernel < kAuto || req_kernel > kGeneric) return DS_ERR_BLOCK;
     KernelKind kind = units > 0 ? kAuto : kGeneric;
     if (req_kernel == kGeneric) kind = kGeneric;
     int waves = kind != kGeneric ? (req_waves ? req_waves : plan_waves(batch * S, di.cus)) : kGW;
-    if (!lds_fits(dtype, n, k, B, B2, S, waves)) {
-        if (waves != kGW && lds_fits(dtype, n, k, B, B2, S, kGW))
+    if (!lds_fits(dtype, n, k, B, B2, S, waves, sorted)) {
+        if (waves != kGW && lds_fits(dtype, n, k, B, B2, S, kGW, sorted))
             waves = kGW;
         else
             return DS_ERR_UNSUPPORTED;
     }
+    // the rows' own kernel sorts its results only when it writes the output
+    const bool sort_here = sorted && S == 1;
     Layout L = make_layout(dtype, n, k, B, B2, S, waves);
+    if (sort_here) L = with_sort(L, k);
     if ((int64_t)L.total > (int64_t)di.lds) return DS_ERR_UNSUPPORTED;
     bool packed = false;  // the ring kernel on packed bfloat16 entries
     if (kind != kGeneric) {
         const bool pk = packed_parts(dtype, n, B, S);
-        const Layout LB = pk ? make_layout(dtype, n, k, B, B2, S, waves, true) : L;
+        Layout LB = L;
+        if (pk) {
+            LB = make_layout(dtype, n, k, B, B2, S, waves, true);
+            if (sort_here) LB = with_sort(LB, k);
+        }
         const Layout LR = with_ring(LB, ceil_div(ceil_div(ceil_div(n, B), S), waves), units, (size_t)di.lds);
         if (req_kernel == kRing && LR.ring_depth == 0) return DS_ERR_UNSUPPORTED;
         if (req_kernel == kRegs || LR.ring_depth == 0) {
@@ -1630,6 +1722,7 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     prm.B = B;
     prm.B2 = B2;
     prm.split = (int32_t)S;
+    prm.sorted = sorted;
     prm.L = L;
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);

@@ -65,6 +65,7 @@ struct Layout {
     uint32_t perm;   // block order (uint16 per block)
     uint32_t misc;   // 16 uint32 of broadcast scratch
     uint32_t ring;   // streaming ring: waves x ring_depth blocks of ring_units KiB (0 if none)
+    uint32_t sort;   // sorted output: next_pow2(k) uint64 sort words (0 if not asked for)
     uint32_t total;  // bytes
     int32_t cap;     // candidate buffer capacity in entries
     int32_t junk;    // first junk entry (cap padded to 8)
@@ -147,6 +148,15 @@ inline Layout with_ring(Layout L, int64_t steps, int units, size_t lds_limit) {
     L.ring_depth = (int32_t)depth;
     L.ring_units = units;
     L.total = (uint32_t)(base + per * depth);
+    return L;
+}
+
+// Room for sorting a row's k results before they are written: next_pow2(k)
+// 64-bit words (key << 32 | ~column).
+inline Layout with_sort(Layout L, int64_t k) {
+    const size_t base = align_up(L.total, 16);
+    L.sort = (uint32_t)base;
+    L.total = (uint32_t)(base + (size_t)next_pow2(k) * 8);
     return L;
 }
 
