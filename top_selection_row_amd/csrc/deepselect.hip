@@ -855,16 +855,27 @@ struct RingStreamer {
 template <class D, int NW, int U>
 __global__ __launch_bounds__(NW * 64) void deepselect_ring_kernel(Params p);
 
-// Descending bitonic sort of the n2 (a power of two) 64-bit words at a: the
-// network of Batcher that "CUDA 算子笔记 4" ("Top K Selection", the bitonic
-// approach) sorts its candidates with. In the stage of distance j, pair q
-// (thread q mod NT) joins word i = q with a zero bit inserted at log2(j) and
-// word i + j. While j < 64 the 64 pairs a wave takes at once stay inside the
-// same 128 words whatever j is, so consecutive such stages need only the
-// wave's own (in-order) LDS accesses; every other stage waits for the
-// workgroup. Starts and ends with a workgroup barrier.
+// Sorted output. Every result becomes one 64-bit word key << 32 | ~column,
+// so plain descending order of the words is the wanted one (keys from the
+// largest down, equal keys by ascending column); padding words are 0, below
+// every result (~column >= 2^31). The words are ordered by Batcher's bitonic
+// network, which "CUDA 算子笔记 4" ("Top K Selection", the bitonic approach)
+// also sorts its candidates with. In the stage of distance j inside runs of
+// `size` words, words i and i ^ j meet; runs whose index has bit `size` clear
+// are ordered descending, the others ascending, and the lower index of a pair
+// ends with the larger word in a descending run.
+__device__ __forceinline__ bool keeps_larger(uint32_t i, uint32_t j, uint32_t size) {
+    return ((i & j) == 0) == ((i & size) == 0);
+}
+
+// Plain form: n2 (a power of two) words in LDS at a. Pair q (thread q mod
+// NT) joins word i = q with a zero bit inserted at log2(j) and word i + j.
+// While j < 64 the 64 pairs a wave takes at once stay inside the same 128
+// words whatever j is, so consecutive such stages need only the wave's own
+// (in-order) LDS accesses; every other stage waits for the workgroup. Starts
+// and ends with a workgroup barrier.
 template <int NW>
-__device__ __forceinline__ void bitonic_desc(uint64_t* a, uint32_t n2) {
+__device__ __forceinline__ void bitonic_lds(uint64_t* a, uint32_t n2) {
     constexpr uint32_t NT = NW * 64;
     const uint32_t half = n2 >> 1;
     bool local = false;  // the previous stage kept to each wave's words
@@ -889,32 +900,151 @@ __device__ __forceinline__ void bitonic_desc(uint64_t* a, uint32_t n2) {
     lds_barrier();
 }
 
-// The row's k results as sort words key << 32 | ~column, descending: keys
-// from the largest down, equal keys by ascending column. Padding words are 0,
-// below every result (~column >= 2^31).
+// A stage of distance J < E inside each thread's E words (i0 = E * thread,
+// so word i0 + e has bit `size` set when i0 or e has).
+template <int E, int J>
+__device__ __forceinline__ void bitonic_in_thread(uint64_t (&v)[E], uint32_t i0, uint32_t size) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if ((e & J) == 0) {
+            const uint64_t x = v[e], y = v[e | J];
+            const bool swap = ((i0 | (uint32_t)e) & size) == 0 ? x < y : x > y;
+            v[e] = swap ? y : x;
+            v[e | J] = swap ? x : y;
+        }
+    }
+}
+
+// The 32-bit word of lane (lane ^ D) of the wave, with vector ALU lane moves
+// only: DPP quad permutes (D = 1, 2), a DPP row shift either way (D = 4), a
+// DPP row rotation by 8 (D = 8, xor 8 inside a 16-lane row), and the gfx950
+// 16- and 32-lane half swaps (D = 16, 32).
+template <int D>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+    if constexpr (D == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    } else if constexpr (D == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    } else if constexpr (D == 4) {
+        const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x104, 0xF, 0xF, false);  // row_shl:4, lane + 4
+        const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x114, 0xF, 0xF, false);  // row_shr:4, lane - 4
+        return (lane_id() & 4) ? dn : up;
+    } else if constexpr (D == 8) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    } else if constexpr (D == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane_id() & 16) ? r[0] : r[1];
+    } else {
+        static_assert(D == 32, "lane distance");
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane_id() & 32) ? r[0] : r[1];
+    }
+}
+
+// A stage of distance j = D * E: word e of this lane meets word e of lane
+// (lane ^ D); all E words of a thread keep the same side.
+template <int E, int D>
+__device__ __forceinline__ void bitonic_lane_stage(uint64_t (&v)[E], uint32_t i0, uint32_t size) {
+    const bool big = keeps_larger(i0, (uint32_t)(D * E), size);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const uint32_t lo = lane_xor<D>((uint32_t)v[e]);
+        const uint32_t hi = lane_xor<D>((uint32_t)(v[e] >> 32));
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        v[e] = (o > v[e]) == big ? o : v[e];
+    }
+}
+
+// Register form: n2 <= E * NT words, thread t holding words E*t .. E*t+E-1
+// in v (threads past n2 / E hold padding). Within a run size, the stages go
+// j = size/2 down to 1: through LDS (buf, n2 words, between workgroup
+// barriers) while j >= 64*E, then across the lanes of the wave with vector
+// lane moves while j >= E, then inside the thread. Waves without a word only
+// take part in the barriers.
+template <int NW, int E>
+__device__ __forceinline__ void bitonic_regs(uint64_t (&v)[E], uint32_t n2, uint64_t* buf) {
+    static_assert(E == 4, "in-thread stages of distance 1 and 2");
+    const uint32_t i0 = threadIdx.x * E;
+    const bool holds = i0 < n2;
+    const bool wave_holds = (uint32_t)wave_id() * 64u * E < n2;
+    if (!wave_holds && n2 <= 64u * E) return;  // no stage through LDS: nothing to join
+    for (uint32_t size = 2; size <= n2; size <<= 1) {
+        uint32_t j = size >> 1;
+        for (; j >= 64u * E; j >>= 1) {
+            lds_barrier();  // the previous stage through LDS has been read
+            if (holds) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) buf[i0 + e] = v[e];
+            }
+            lds_barrier();
+            if (holds) {
+                const bool big = keeps_larger(i0, j, size);  // the same for the thread's E words
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const uint64_t o = buf[(i0 + e) ^ j];
+                    v[e] = (o > v[e]) == big ? o : v[e];
+                }
+            }
+        }
+        if (!wave_holds) continue;
+        if (j == 32u * E) bitonic_lane_stage<E, 32>(v, i0, size), j >>= 1;
+        if (j == 16u * E) bitonic_lane_stage<E, 16>(v, i0, size), j >>= 1;
+        if (j == 8u * E) bitonic_lane_stage<E, 8>(v, i0, size), j >>= 1;
+        if (j == 4u * E) bitonic_lane_stage<E, 4>(v, i0, size), j >>= 1;
+        if (j == 2u * E) bitonic_lane_stage<E, 2>(v, i0, size), j >>= 1;
+        if (j == 1u * E) bitonic_lane_stage<E, 1>(v, i0, size), j >>= 1;
+        if (j == 2u) bitonic_in_thread<E, 2>(v, i0, size), j >>= 1;
+        if (j == 1u) bitonic_in_thread<E, 1>(v, i0, size);
+    }
+}
+
+// Sort word of the row's result j (j < k).
+template <class D>
+__device__ __forceinline__ uint64_t sort_word(const Lds<D>& s, uint32_t j) {
+    uint32_t key, col;
+    if constexpr (is_packed<D>::value) {
+        const uint32_t e = s.keys[j];
+        key = e >> 16;
+        col = e & 0xFFFFu;
+    } else {
+        key = s.keys[j];
+        col = s.idx[j];
+    }
+    return ((uint64_t)key << 32) | (uint32_t)~col;
+}
+
+template <class D>
+__device__ __forceinline__ void put_sorted(const Params& p, int64_t row, uint32_t j, uint64_t w) {
+    const int64_t k = p.k;
+    const uint32_t key = (uint32_t)(w >> 32);
+    if constexpr (D::kBytes == 4)
+        reinterpret_cast<uint32_t*>(p.out_vals)[row * k + j] = D::raw(key);
+    else
+        reinterpret_cast<uint16_t*>(p.out_vals)[row * k + j] = (uint16_t)D::raw(key);
+    p.out_idx[row * k + j] = (int32_t)~(uint32_t)w;
+}
+
+// Write the row's k results in descending order.
 template <class D, int NW>
-__device__ __forceinline__ const uint64_t* sort_results(Lds<D>& s, const Params& p) {
-    uint64_t* a = reinterpret_cast<uint64_t*>(s.base + p.L.sort);
+__device__ __forceinline__ void write_sorted(Lds<D>& s, const Params& p, int64_t row) {
+    constexpr int E = 4;
+    uint64_t* buf = reinterpret_cast<uint64_t*>(s.base + p.L.sort);
     const uint32_t k = (uint32_t)p.k;
     const uint32_t n2 = k <= 1u ? 1u : 1u << (32 - __clz(k - 1u));
-    for (uint32_t j = threadIdx.x; j < n2; j += NW * 64) {
-        uint64_t w = 0;
-        if (j < k) {
-            uint32_t key, col;
-            if constexpr (is_packed<D>::value) {
-                const uint32_t e = s.keys[j];
-                key = e >> 16;
-                col = e & 0xFFFFu;
-            } else {
-                key = s.keys[j];
-                col = s.idx[j];
-            }
-            w = ((uint64_t)key << 32) | (uint32_t)~col;
-        }
-        a[j] = w;
+    if (n2 <= (uint32_t)(E * NW * 64)) {
+        const uint32_t i0 = threadIdx.x * E;
+        uint64_t v[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = i0 + e < k ? sort_word<D>(s, i0 + e) : 0ull;
+        bitonic_regs<NW, E>(v, n2, buf);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (i0 + e < k) put_sorted<D>(p, row, i0 + e, v[e]);
+    } else {
+        for (uint32_t j = threadIdx.x; j < n2; j += NW * 64) buf[j] = j < k ? sort_word<D>(s, j) : 0ull;
+        bitonic_lds<NW>(buf, n2);
+        for (uint32_t j = threadIdx.x; j < k; j += NW * 64) put_sorted<D>(p, row, j, buf[j]);
     }
-    bitonic_desc<NW>(a, n2);
-    return a;
 }
 
 template <class D, int NW>
@@ -922,16 +1052,7 @@ __device__ __forceinline__ void write_row(Lds<D>& s, const Params& p, int64_t ro
                                           uint64_t R, uint64_t maxlen) {
     const int64_t k = p.k;
     if (p.sorted) {
-        const uint64_t* a = sort_results<D, NW>(s, p);
-        for (int64_t j = threadIdx.x; j < k; j += NW * 64) {
-            const uint64_t w = a[j];
-            const uint32_t key = (uint32_t)(w >> 32);
-            if constexpr (D::kBytes == 4)
-                reinterpret_cast<uint32_t*>(p.out_vals)[row * k + j] = D::raw(key);
-            else
-                reinterpret_cast<uint16_t*>(p.out_vals)[row * k + j] = (uint16_t)D::raw(key);
-            p.out_idx[row * k + j] = (int32_t)~(uint32_t)w;
-        }
+        write_sorted<D, NW>(s, p, row);
     } else if constexpr (is_packed<D>::value) {
         // one part per row: the entry's column is the row's
         for (int64_t j = threadIdx.x; j < k; j += NW * 64) {
