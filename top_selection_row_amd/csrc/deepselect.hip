@@ -69,7 +69,7 @@ struct RunState {
     uint64_t W = 0;     // RadixSelectTopK input (can pass 2^32 for huge k / tiny B2)
     uint32_t A = 0, R = 0, maxlen = 0;
     uint32_t par = 0;   // count-buffer parity
-    uint32_t kmax = 0;  // this wave's largest appended key
+    uint32_t kmax = 0;  // the largest key this lane appended (reduced over the wave at a select)
 };
 
 template <class D>
@@ -80,7 +80,6 @@ struct Lds {
     uint32_t* fold;
     uint32_t* tot;
     uint32_t* gathered;
-    uint32_t* sparse;   // 64 words per wave (ring streaming: few-survivor scatter)
     uint32_t* cnt;
     uint16_t* perm;
     uint32_t* misc;  // [2] gathered-key counter, [8 + w] wave w's largest appended key
@@ -98,7 +97,6 @@ __device__ __forceinline__ Lds<D> lds_of(unsigned char* smem, const Layout& L) {
     s.fold = reinterpret_cast<uint32_t*>(smem + L.fold);
     s.tot = reinterpret_cast<uint32_t*>(smem + L.tot);
     s.gathered = reinterpret_cast<uint32_t*>(smem + L.gather);
-    s.sparse = reinterpret_cast<uint32_t*>(smem + L.sparse);
     s.cnt = reinterpret_cast<uint32_t*>(smem + L.cnt);
     s.perm = reinterpret_cast<uint16_t*>(smem + L.perm);
     s.misc = reinterpret_cast<uint32_t*>(smem + L.misc);
@@ -113,12 +111,12 @@ __device__ __forceinline__ void begin_item(Lds<D>& s) {
     clear_words<NW>(s.hist, kHistWords);
 }
 
-// Fold the largest key this wave appended into its running maximum; the top
-// of the key range the radix select starts from is the largest over the
-// waves. A register, not an LDS atomic: the compiler makes every LDS atomic
-// wait for the wave's ring loads still in flight.
+// Fold the largest key this lane appended into its running maximum. The top
+// of the key range the radix select starts from is the largest over the lanes
+// and waves; it is reduced only when a select needs it. A register, not an LDS
+// atomic: the compiler makes every LDS atomic wait for the wave's ring loads
+// still in flight.
 __device__ __forceinline__ void publish_max(RunState& st, uint32_t kmax) {
-    kmax = wave_max(kmax);
     st.kmax = kmax > st.kmax ? kmax : st.kmax;
 }
 
@@ -128,7 +126,8 @@ template <class D, int NW>
 __device__ __forceinline__ void select_buffer(Lds<D>& s, RunState& st, uint32_t k) {
     static_assert(NW <= 8, "one largest-key cell per wave in misc[8..16)");
     const uint32_t lo = st.tset ? st.tkey : 0u;
-    if (lane_id() == 0) s.misc[8 + wave_id()] = st.kmax;
+    const uint32_t wmax = wave_max(st.kmax);
+    if (lane_id() == 0) s.misc[8 + wave_id()] = wmax;
     lds_barrier();  // appends and the waves' largest keys are visible
     uint32_t hi = 0;
 #pragma unroll
@@ -641,43 +640,29 @@ struct RingStreamer {
         publish_max(st, kmax);
     }
 
-    // Few survivors in the wave (c <= 64): survivor j is written by lane j.
-    // Every lane lists its survivors in the wave's scratch (lane id and rank
-    // inside the lane, at its exclusive prefix excl), then lane j takes entry
-    // j, fetches that lane's mask with a lane permute, finds the element of
-    // that rank and reads it back from the block's ring slot.
-    __device__ __forceinline__ void scatter_sparse(uint32_t m, uint32_t excl, uint32_t lc, uint32_t c,
-                                                   uint32_t base, uint32_t boff, const u32x4* slot,
-                                                   uint32_t* scratch) const {
+    // Few survivors in the wave (c <= 64): every lane walks its own admitted
+    // elements (mask m) lowest first and appends each at pos, reading its raw
+    // bits back from the block's ring slot (the loop runs as often as the
+    // lane with the most survivors needs).
+    __device__ __forceinline__ void scatter_few(uint32_t m, uint32_t pos, uint32_t boff, const u32x4* slot) const {
         uint32_t lane = lane_id();
         asm volatile("" : "+v"(lane));
-        for (uint32_t t = 0; t < lc; ++t) scratch[excl + t] = (lane << 8) | t;
-        const uint32_t ent = lane < c ? scratch[lane] : 0u;
-        const uint32_t src = ent >> 8, rank = ent & 255u;
-        // every lane takes part in the permute (a lane outside it would not
-        // provide its mask)
-        uint32_t mm = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(src << 2), (int)m);
-        uint32_t key = 0;
-        if (lane < c) {
-            // position of the set bit of that rank (from bit 0)
-            uint32_t e = 0, rr = rank;
-#pragma unroll
-            for (int wdt = 16; wdt >= 1; wdt >>= 1) {
-                const uint32_t low = (uint32_t)__builtin_popcount(mm & ((1u << wdt) - 1u));
-                if (rr >= low) {
-                    rr -= low;
-                    mm >>= wdt;
-                    e += wdt;
-                }
-            }
+        const unsigned char* lp = reinterpret_cast<const unsigned char*>(slot + lane);
+        const uint32_t col0 = boff + lane * V;
+        uint32_t kmax = 0;
+        while (m != 0u) {
+            const uint32_t e = (uint32_t)__builtin_ctz(m);
+            m &= m - 1u;
             const uint32_t u = e / V, q = e % V;
-            const unsigned char* p = reinterpret_cast<const unsigned char*>(slot + u * 64 + src) + q * D::kBytes;
+            const unsigned char* p = lp + u * (64 * 16) + q * D::kBytes;
             const uint32_t raw = D::kBytes == 4 ? *reinterpret_cast<const uint32_t*>(p)
                                                 : (uint32_t)*reinterpret_cast<const uint16_t*>(p);
-            key = D::key(raw);
-            put(base + lane, key, boff + u * UE + src * V + q);
+            const uint32_t key = D::key(raw);
+            put(pos, key, col0 + u * UE + q);
+            ++pos;
+            kmax = key > kmax ? key : kmax;
         }
-        publish_max(st, key);  // every lane takes part in the reduction
+        publish_max(st, kmax);
     }
 
     // Append a whole full block at pos (before the first compaction, when
@@ -784,7 +769,7 @@ struct RingStreamer {
                 else
                     scatter_valid(r, pos, boff, blen);
             } else if (kMasks && c <= 64u) {
-                scatter_sparse(lm, incl - lc, lc, c, my_base, boff, slot, s.sparse + w * 64);
+                scatter_few(lm, pos, boff, slot);
             } else if (kMasks) {
                 if (th.neg)
                     scatter_dense<false>(r, lm, pos, boff);

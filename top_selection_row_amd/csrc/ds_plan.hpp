@@ -59,7 +59,6 @@ struct Layout {
     uint32_t hist;   // radix histogram: 16 copies of 256 16-bit counters (8 KiB)
     uint32_t fold;   // 256 folded bins (uint32)
     uint32_t gather; // kGather keys of one radix bin (uint32), gathered for a wave-local finish
-    uint32_t sparse; // 64 uint32 per wave: survivor list of a wave with few survivors
     uint32_t tot;    // 2 x rounds x waves per-wave totals of the select partition
     uint32_t cnt;    // 2 x waves per-wave counts (block loop)
     uint32_t perm;   // block order (uint16 per block)
@@ -100,8 +99,6 @@ inline Layout make_layout_raw(int key_bytes, int64_t cap, int64_t order_n, int w
     off += 256 * 4;
     L.gather = (uint32_t)off;
     off += kGather * 4;
-    L.sparse = (uint32_t)off;
-    off += (size_t)waves * 64 * 4;
     L.tot = (uint32_t)off;
     off += align_up((size_t)2 * kRoundsPerGroup * waves * 4, 16);
     L.cnt = (uint32_t)off;
