@@ -119,6 +119,9 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--sorted", action="store_true",
                     help="results of each row in descending order (ds_options_t.sorted)")
+    ap.add_argument("--lengths", action="store_true",
+                    help="pass each row's valid length (ds_options_t.lengths; causal rows end where their "
+                         "-inf tail starts, other workloads are full rows)")
     ap.add_argument("--rotate-mb", type=int, default=768)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -173,7 +176,9 @@ def main() -> int:
         log(f"[bench] no valid split: {ds.deepselect_status_string(split)}")
         return 1
     lib = ds.library()
-    opt = ds.DsOptions(int(split), int(args.waves), None, None, 0, int(args.kernel), int(args.sorted))
+    lens = torch.from_numpy(synth.valid_lengths(args.workload)).to(dev) if args.lengths else None
+    opt = ds.DsOptions(int(split), int(args.waves), None, None, 0, int(args.kernel), int(args.sorted),
+                       lens.data_ptr() if lens is not None else None)
     ptrs = [rot[i].data_ptr() for i in range(copies)]
     vptr, iptr = vals.data_ptr(), idx.data_ptr()
     fn = lib.deepselect_topk_ex
@@ -212,7 +217,9 @@ def main() -> int:
     ms_per_step = region_ms / K
     elems = w.batch * w.n
     value = elems / (ms_per_step * 1e-3) / 1e9
-    alg_bytes = w.batch * w.n * es + w.batch * w.k * (es + 4)
+    # bytes the call must move: every (valid) input element once, and the output
+    read_elems = int(lens.sum().item()) if lens is not None else w.batch * w.n
+    alg_bytes = read_elems * es + w.batch * w.k * (es + 4)
     achieved = alg_bytes / (kern_avg_ms * 1e-3) / 1e9
     log(f"[bench] region {region_ms:.3f} ms for {K} steps (wall {wall * 1e3:.1f} ms); kernel avg "
         f"{kern_avg_ms * 1e3:.2f} us, median {kern_med_ms * 1e3:.2f} us; {achieved:.0f} GB/s")
@@ -240,8 +247,8 @@ def main() -> int:
         cpu = cpu_baseline(args.workload, args.cpu_seconds)
         log(f"[bench] cpu oracle: {cpu}")
 
-    # the committed counter figures are for the unsorted call
-    traffic = None if args.sorted else measured_traffic(args.workload)
+    # the committed counter figures are for the plain call
+    traffic = None if (args.sorted or args.lengths) else measured_traffic(args.workload)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -257,6 +264,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": w.batch, "N": w.n, "input_dtype": w.dtype,
                    "k": w.k, "B": w.block, "B2": w.block2, "split": int(split), "sorted": bool(args.sorted),
+                   "lengths": bool(args.lengths),
                    "rotating_copies": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

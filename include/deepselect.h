@@ -104,6 +104,18 @@ typedef struct ds_options {
      * LDS, so a shape near the limit may give DS_ERR_UNSUPPORTED. The result
      * set is the same either way. Any other value: DS_ERR_BLOCK. */
     int32_t sorted;
+    /* Device pointer to batch int32 valid lengths, or NULL (every row has N).
+     * Row r is then the prefix x[r*row_stride .. r*row_stride + L_r), with
+     * L_r = lengths[r] clamped to [0, N]: DeepSelect runs on it exactly as on a
+     * row of L_r elements (its ceil(L_r/B) blocks, cut into the call's split;
+     * a part may get fewer than k elements or none), and nothing past it takes
+     * part (for example a causal sparse-attention row, which covers only the
+     * positions before its query: the use of the deep-dive's section
+     * "算法设计背景"). When L_r < k the row's first L_r outputs are its
+     * elements and the other k - L_r are fillers: index -1 with the bits of
+     * negative infinity. Statistics count what the prefix costs. The array is
+     * read by the kernels; the library does not check it on the host. */
+    const int32_t *lengths;
 } ds_options_t;
 
 /* Check arguments only (pure host code, no HIP call; usable without a GPU).
@@ -117,7 +129,7 @@ int deepselect_topk(const void *x, int dtype, int64_t batch, int64_t N, int64_t 
                     int32_t *out_idx, void *stream);
 
 /* deepselect_topk with options (forced split, statistics, caller workspace,
- * sorted output).
+ * sorted output, per-row valid lengths).
  * opt may be NULL (then identical to deepselect_topk). */
 int deepselect_topk_ex(const void *x, int dtype, int64_t batch, int64_t N, int64_t row_stride,
                        int32_t k, int32_t B, int32_t B2, uint64_t seed, void *out_vals,

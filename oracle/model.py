@@ -224,16 +224,27 @@ def part_bounds(m: int, split: int):
 
 
 def row_topk(x_row: np.ndarray, k: int, block: int, block2: int, seed: int = 0, row: int = 0,
-             split: int = 1) -> RowResult:
-    """DeepSelect on one row (float32 values or raw bfloat16 bits), S parts plus merge."""
+             split: int = 1, length: int | None = None) -> RowResult:
+    """DeepSelect on one row (float32 values or raw bfloat16 bits), S parts plus merge.
+
+    ``length``: the row's valid length (clamped to [0, N]). The method then
+    runs on the prefix x_row[:length] as on a row of that many elements: its
+    blocks cut into ``split`` parts (some may hold fewer than k elements, or
+    none), each part's result, and the merge over the parts' results. With
+    fewer than k valid elements every one of them is returned.
+    """
     raw, dt = raw_bits(np.asarray(x_row))
     bits = 32 if dt == F32 else 16
+    if length is not None:
+        raw = raw[:min(max(int(length), 0), len(raw))]
     keys = key_of(raw)
     n = len(keys)
-    if not (1 <= k <= n and block >= 1 and block2 >= 1):
-        raise ValueError("DeepSelectTopk requires 1 <= k <= N, B >= 1, B2 >= 1")
+    if not (k >= 1 and block >= 1 and block2 >= 1):
+        raise ValueError("DeepSelectTopk requires k >= 1, B >= 1, B2 >= 1")
+    if length is None and k > n:
+        raise ValueError("DeepSelectTopk requires k <= N")
     m = -(-n // block)
-    if not 1 <= split <= m:
+    if split < 1 or (length is None and split > m):
         raise ValueError("split must be in [1, ceil(N/B)]")
     reads = np.zeros(n, dtype=np.int64)
     total = RunStats()
@@ -263,9 +274,10 @@ def expected_w_bound(n: int, k: int, block: int, block2: int) -> float:
 
 
 def batch_topk(x: np.ndarray, k: int, block: int, block2: int, seed: int = 0, split: int = 1,
-               row0: int = 0):
+               row0: int = 0, lengths=None):
     """Model over every row of ``x``; ``row0`` is the row number of x[0] (block order)."""
-    out = [row_topk(x[i], k, block, block2, seed, row0 + i, split) for i in range(x.shape[0])]
+    out = [row_topk(x[i], k, block, block2, seed, row0 + i, split,
+                    None if lengths is None else int(lengths[i])) for i in range(x.shape[0])]
     return out
 
 

@@ -119,6 +119,20 @@ def _row(w: Workload, r: int) -> np.ndarray:
     raise ValueError(f"unknown generator family {w.kind!r}")
 
 
+def valid_lengths(name: str, rows=None) -> np.ndarray:
+    """Per-row valid length (int32) of workload ``name``: where a causal row's
+    -inf tail starts, N for every other family. The same draws as the rows."""
+    w = WORKLOADS[name]
+    rows = list(range(w.batch) if rows is None else rows)
+    out = np.full(len(rows), w.n, dtype=np.int32)
+    if w.kind == "causal":
+        for i, r in enumerate(rows):
+            rng = np.random.default_rng((w.data_seed, r))
+            rng.standard_normal(w.n, dtype=np.float32)
+            out[i] = int(rng.integers(2048, w.n, endpoint=True))
+    return out
+
+
 def generate_rows(name: str, rows=None) -> np.ndarray:
     """Rows of workload ``name`` as a [len(rows), N] array (all rows if None)."""
     w = WORKLOADS[name]

@@ -349,3 +349,81 @@ def test_sorted_output(case):
     assert np.array_equal(st, u_st)
     for r in range(rows):
         assert np.array_equal(np.sort(idx[r]), np.sort(u_idx[r]))
+
+
+# ---------------------------------------------------------------- per-row valid lengths
+
+def run_gpu_len(x: np.ndarray, k, B, B2, lengths, seed=0, split=0, waves=0, kernel=0, sorted=False):
+    xt = to_device(x)
+    lt = torch.from_numpy(np.asarray(lengths, dtype=np.int32)).to(DEV)
+    out = ds.topk(xt, k, B, B2, seed, split=split, stats=True, waves=waves, kernel=kernel, sorted=sorted,
+                  lengths=lt)
+    torch.cuda.synchronize()
+    return raw_of(out[0]), out[1].cpu().numpy(), out[2].cpu().numpy()
+
+
+def check_rows_len(x: np.ndarray, vals, idx, k, lengths, sorted=False):
+    """Row r against the oracle on its prefix x[r, :L_r] (L_r clamped to
+    [0, N]); outputs past min(k, L_r) are fillers (-1, negative infinity)."""
+    n = x.shape[1]
+    neg_inf = 0xFF800000 if x.dtype == np.float32 else 0xFF80
+    for r in range(x.shape[0]):
+        L = min(max(int(lengths[r]), 0), n)
+        c = min(k, L)
+        assert np.all(idx[r][c:] == -1), f"row {r}: filler index"
+        assert np.all(vals[r][c:] == neg_inf), f"row {r}: filler value"
+        if c == 0:
+            continue
+        sub = np.ascontiguousarray(x[r:r + 1, :L])
+        if sorted:
+            check_sorted_rows(sub, vals[r:r + 1, :c], idx[r:r + 1, :c], c)
+        else:
+            check_rows(sub, vals[r:r + 1, :c], idx[r:r + 1, :c], c)
+
+
+def check_stats_len(x, st, k, B, B2, seed, split, lengths, rows):
+    for r in rows:
+        res = model.row_topk(x[r], k, B, B2, seed=seed, row=r, split=split, length=int(lengths[r]))
+        want = (res.stats.W, res.stats.A, res.stats.R, res.stats.max_len)
+        assert tuple(int(v) for v in st[r]) == want, f"row {r}: (W, A, R, max_len) {tuple(st[r])} != model {want}"
+
+
+@pytest.mark.parametrize("split,waves,kernel", [(1, 8, 1), (2, 8, 1), (4, 4, 1), (2, 8, 2), (2, 4, 3)])
+def test_causal_lengths(split, waves, kernel):
+    # the causal rows with their valid lengths: the top-k of each prefix
+    w = synth.WORKLOADS["dsa128k_bf16"]
+    rows = 8
+    log(f"[gpu] causal lengths dsa128k_bf16 S={split} waves={waves} kernel {KERNELS[kernel]}")
+    x = synth.generate("dsa128k_bf16", rows)
+    L = synth.valid_lengths("dsa128k_bf16", range(rows))
+    vals, idx, st = run_gpu_len(x, w.k, w.block, w.block2, L, seed=5, split=split, waves=waves, kernel=kernel)
+    check_rows_len(x, vals, idx, w.k, L)
+    check_stats_len(x, st, w.k, w.block, w.block2, 5, split, L, range(4))
+
+
+LEN_EDGE = [0, 1, 7, 95, 96, 97, 255, 257, 600, 515, 4999, 5000, 5050, -4]
+
+
+@pytest.mark.parametrize("dt,split,kernel,srt", [("f32", 1, 0, False), ("bf16", 1, 0, False), ("f32", 3, 0, False),
+                                                 ("bf16", 3, 0, True), ("f32", 2, 2, True), ("bf16", 2, 3, False),
+                                                 ("f32", 1, 3, True)])
+def test_edge_lengths(dt, split, kernel, srt):
+    # lengths of every kind in one call: none, fewer than k, ragged inside a
+    # 16-byte load, fewer blocks than parts, N, past N and negative (clamped)
+    n, k, B, B2 = 5000, 96, 256, 128
+    rows = len(LEN_EDGE)
+    log(f"[gpu] edge lengths {dt} S={split} kernel {KERNELS.get(kernel, 'auto')} sorted={srt}")
+    x = synth.random_rows(rows, n, dt, 41, "gauss")
+    vals, idx, st = run_gpu_len(x, k, B, B2, LEN_EDGE, seed=3, split=split, kernel=kernel, sorted=srt)
+    check_rows_len(x, vals, idx, k, LEN_EDGE, sorted=srt)
+    check_stats_len(x, st, k, B, B2, 3, split, LEN_EDGE, range(rows))
+
+
+def test_full_lengths_equal_the_plain_call():
+    w = synth.WORKLOADS["dsa32k"]
+    x = synth.generate("dsa32k", 8)
+    log("[gpu] lengths = N against no lengths")
+    a = run_gpu(x, w.k, w.block, w.block2, seed=2, split=2)
+    b = run_gpu_len(x, w.k, w.block, w.block2, [w.n] * 8, seed=2, split=2)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)

@@ -208,3 +208,61 @@ def test_block_order_changes_cost_not_result():
     assert sorted(ci.tolist()) == list(range(len(asc) - 512, len(asc)))
     rnd = model.row_topk(asc, 512, 1024, 1024, seed=0)
     assert st.W > 10 * rnd.stats.W
+
+
+# ---------------------------------------------------------------- per-row valid lengths
+
+def _prefix_check(x_row, length, k, res):
+    """The model on a prefix against the oracle's plain top-k of that prefix."""
+    n_valid = min(max(int(length), 0), len(x_row))
+    c = min(k, n_valid)
+    assert len(res.idx) == c
+    if c == 0:
+        return
+    sub = np.ascontiguousarray(x_row[:n_valid])[None, :]
+    o_vals, _ = oracle.topk(sub, c)
+    assert np.all(res.idx < n_valid) and len(np.unique(res.idx)) == c
+    assert np.array_equal(np.sort(oracle.keys(res.vals)), np.sort(oracle.keys(o_vals[0])))
+
+
+@pytest.mark.parametrize("split", [1, 3])
+def test_valid_length_prefix_matches_oracle(split):
+    # the method on x[:L] for lengths across the edge cases: none, one
+    # element, fewer than k, a ragged last block, fewer blocks than parts,
+    # all of N, past N (clamped) and negative (clamped to 0)
+    n, k, B, B2 = 5000, 96, 256, 128
+    x = synth.random_rows(1, n, "f32", 5, "gauss")[0]
+    for L in [0, 1, 7, k - 1, k, k + 1, 255, 257, 600, 2 * 256 + 3, n, n + 50, -4]:
+        res = model.row_topk(x, k, B, B2, seed=2, row=0, split=split, length=L)
+        _prefix_check(x, L, k, res)
+        st = res.stats
+        assert st.W == st.A + k * st.R  # per call, so also summed over parts and merge
+        assert st.A <= max(0, min(L, n)) + (split > 1) * split * k
+        if min(max(L, 0), n) == 0:
+            assert (st.W, st.A, st.R, st.max_len) == (0, 0, 0, 0)
+
+
+def test_valid_length_n_is_the_plain_row():
+    w = synth.WORKLOADS["dsa32k"]
+    x = synth.generate("dsa32k", 2)
+    for split in (1, 2):
+        a = model.row_topk(x[1], w.k, w.block, w.block2, seed=4, row=1, split=split)
+        b = model.row_topk(x[1], w.k, w.block, w.block2, seed=4, row=1, split=split, length=w.n)
+        assert np.array_equal(a.idx, b.idx)
+        assert (a.stats.W, a.stats.A, a.stats.R, a.stats.max_len) == \
+            (b.stats.W, b.stats.A, b.stats.R, b.stats.max_len)
+
+
+def test_causal_lengths_mark_the_minus_inf_tail():
+    # the lengths the causal workload is drawn with: finite values before,
+    # -inf from there on, so the prefix holds every finite value of the row
+    x = synth.generate("dsa128k_bf16", 5)
+    L = synth.valid_lengths("dsa128k_bf16", range(5))
+    for r in range(5):
+        assert np.all(x[r, L[r]:] == 0xFF80)
+        assert x[r, L[r] - 1] != 0xFF80
+        assert 2048 <= L[r] <= x.shape[1]
+    w = synth.WORKLOADS["dsa128k_bf16"]
+    for r in range(2):
+        res = model.row_topk(x[r], w.k, w.block, w.block2, seed=0, row=r, split=2, length=L[r])
+        _prefix_check(x[r], L[r], w.k, res)

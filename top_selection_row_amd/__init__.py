@@ -35,7 +35,7 @@ class DsOptions(ctypes.Structure):
     _fields_ = [("split", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("stats", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("kernel", ctypes.c_int32),
-                ("sorted", ctypes.c_int32)]
+                ("sorted", ctypes.c_int32), ("lengths", ctypes.c_void_p)]
 
 
 _lib = None
@@ -122,16 +122,28 @@ def deepselect_topk(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals, ou
 
 def deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals, out_idx, stream,
                        split=0, stats=None, workspace=None, workspace_bytes=0, waves=0, kernel=0,
-                       sorted=0) -> int:
-    opt = DsOptions(int(split), int(waves), stats, workspace, int(workspace_bytes), int(kernel), int(sorted))
+                       sorted=0, lengths=None) -> int:
+    opt = DsOptions(int(split), int(waves), stats, workspace, int(workspace_bytes), int(kernel), int(sorted),
+                    lengths)
     return library().deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed & (2**64 - 1),
                                         out_vals, out_idx, stream, ctypes.byref(opt))
 
 
 # ---------------------------------------------------------------- torch wrapper
 
+def _lengths_ptr(lengths, x, batch):
+    if lengths is None:
+        return None
+    import torch
+
+    if (lengths.dtype != torch.int32 or lengths.device != x.device or lengths.dim() != 1
+            or lengths.shape[0] != batch or not lengths.is_contiguous()):
+        raise ValueError("lengths must be a contiguous int32 tensor of batch entries on x's device")
+    return lengths.data_ptr()
+
+
 def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, waves: int = 0,
-         kernel: int = 0, stats: bool = False, sorted: bool = False, out=None, stream=None):
+         kernel: int = 0, stats: bool = False, sorted: bool = False, lengths=None, out=None, stream=None):
     """Row-wise top-k of a 2-D CUDA tensor (float32 or bfloat16, unit column stride).
 
     ``kernel``: 0 library choice, 1 ring streaming, 2 register streaming,
@@ -140,7 +152,10 @@ def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, waves: in
     Returns (vals [batch, k] same dtype, idx [batch, k] int32) and, with
     ``stats=True``, a [batch, 4] int64 tensor (W, A, R, max_len). The k entries
     of a row are in no particular order, or with ``sorted=True`` largest first
-    (equal values by ascending column). Raises on any rejected argument.
+    (equal values by ascending column). ``lengths``: an optional int32 device
+    tensor of ``batch`` valid row lengths (``ds_options_t.lengths``: row r is
+    its first lengths[r] elements; outputs past a row shorter than k are index
+    -1 with value -inf). Raises on any rejected argument.
     """
     import torch
 
@@ -168,7 +183,7 @@ def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, waves: in
         _check(deepselect_topk_ex(x.data_ptr(), dt, batch, n, row_stride, k, B, B2, seed,
                                   vals.data_ptr(), idx.data_ptr(), stream, split=split, waves=waves,
                                   kernel=kernel, stats=st.data_ptr() if st is not None else None,
-                                  sorted=int(bool(sorted))))
+                                  sorted=int(bool(sorted)), lengths=_lengths_ptr(lengths, x, batch)))
     if stats:
         return vals, idx, st
     return vals, idx

@@ -59,6 +59,7 @@ struct Params {
     uint64_t seed;
     int32_t k, B, B2, split;
     int32_t sorted;  // write each row's results in descending order
+    const int32_t* lengths;  // per-row valid lengths (NULL: every row has n)
     Layout L;
 };
 
@@ -227,18 +228,30 @@ struct Streamer {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t e0 = u * UE + lane * V;
-            const uint32_t off = e0 + V <= blen ? (boff + e0) * D::kBytes : kOob;
+            const uint32_t off = e0 < blen ? (boff + e0) * D::kBytes : kOob;
             r.v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
         }
     }
 
-    // Lanes past the end of a short block read zeros; give them all-ones bits
-    // instead, whose key is 0: never above any threshold.
+    // Elements past the end of a short block (whole 16-byte loads, or the
+    // tail of the load that holds the end) get all-ones bits, whose key is 0:
+    // never above any threshold.
     __device__ __forceinline__ void mask_tail(BlockRegs<U>& r, uint32_t blen) const {
         const uint32_t lane = lane_id();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (u * UE + lane * V >= blen) r.v[u] = u32x4{~0u, ~0u, ~0u, ~0u};
+            const uint32_t e0 = u * UE + lane * V;
+            const uint32_t nv = e0 < blen ? blen - e0 : 0u;  // the lane's elements inside the block
+            if (nv < (uint32_t)V) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    if constexpr (V == 4)
+                        r.v[u][w] |= (uint32_t)w >= nv ? ~0u : 0u;
+                    else
+                        r.v[u][w] |= ((uint32_t)(2 * w) >= nv ? 0xFFFFu : 0u) |
+                                     ((uint32_t)(2 * w + 1) >= nv ? 0xFFFF0000u : 0u);
+                }
+            }
         }
     }
 
@@ -472,7 +485,7 @@ struct RingStreamer {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t e0 = u * UE + lane * V;
-            const uint32_t off = e0 + V <= blen ? (boff + e0) * D::kBytes : kOob;
+            const uint32_t off = e0 < blen ? (boff + e0) * D::kBytes : kOob;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc, (__attribute__((address_space(3))) void*)(ring + (q * U + u) * 64), 16, off, 0, 0, 0);
         }
@@ -496,13 +509,25 @@ struct RingStreamer {
         for (int u = 0; u < U; ++u) r.v[u] = ring[(q * U + u) * 64 + lane];
     }
 
-    // Lanes past the end of a short block hold zeros; give them all-ones bits
-    // instead, whose key is 0: never above any threshold.
+    // Elements past the end of a short block (whole 16-byte loads, or the
+    // tail of the load that holds the end) get all-ones bits, whose key is 0:
+    // never above any threshold.
     __device__ __forceinline__ void mask_tail(BlockRegs<U>& r, uint32_t blen) const {
         const uint32_t lane = lane_id();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (u * UE + lane * V >= blen) r.v[u] = u32x4{~0u, ~0u, ~0u, ~0u};
+            const uint32_t e0 = u * UE + lane * V;
+            const uint32_t nv = e0 < blen ? blen - e0 : 0u;  // the lane's elements inside the block
+            if (nv < (uint32_t)V) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    if constexpr (V == 4)
+                        r.v[u][w] |= (uint32_t)w >= nv ? ~0u : 0u;
+                    else
+                        r.v[u][w] |= ((uint32_t)(2 * w) >= nv ? 0xFFFFu : 0u) |
+                                     ((uint32_t)(2 * w + 1) >= nv ? 0xFFFF0000u : 0u);
+                }
+            }
         }
     }
 
@@ -998,20 +1023,33 @@ __device__ __forceinline__ uint64_t sort_word(const Lds<D>& s, uint32_t j) {
     return ((uint64_t)key << 32) | (uint32_t)~col;
 }
 
+// Output entry j of a row: a result (raw bits, column), or past a short row's
+// results the filler: index -1 with the bits of negative infinity.
 template <class D>
-__device__ __forceinline__ void put_sorted(const Params& p, int64_t row, uint32_t j, uint64_t w) {
+__device__ __forceinline__ void put_out(const Params& p, int64_t row, uint32_t j, uint32_t raw, int32_t col) {
     const int64_t k = p.k;
-    const uint32_t key = (uint32_t)(w >> 32);
     if constexpr (D::kBytes == 4)
-        reinterpret_cast<uint32_t*>(p.out_vals)[row * k + j] = D::raw(key);
+        reinterpret_cast<uint32_t*>(p.out_vals)[row * k + j] = raw;
     else
-        reinterpret_cast<uint16_t*>(p.out_vals)[row * k + j] = (uint16_t)D::raw(key);
-    p.out_idx[row * k + j] = (int32_t)~(uint32_t)w;
+        reinterpret_cast<uint16_t*>(p.out_vals)[row * k + j] = (uint16_t)raw;
+    p.out_idx[row * k + j] = col;
+}
+template <class D>
+__device__ __forceinline__ void put_filler(const Params& p, int64_t row, uint32_t j) {
+    put_out<D>(p, row, j, D::kBytes == 4 ? 0xFF800000u : 0xFF80u, -1);
 }
 
-// Write the row's k results in descending order.
+template <class D>
+__device__ __forceinline__ void put_sorted(const Params& p, int64_t row, uint32_t j, uint64_t w, uint32_t cnt) {
+    if (j < cnt)
+        put_out<D>(p, row, j, D::raw((uint32_t)(w >> 32)), (int32_t)~(uint32_t)w);
+    else
+        put_filler<D>(p, row, j);
+}
+
+// Write the row's cnt results in descending order (then k - cnt fillers).
 template <class D, int NW>
-__device__ __forceinline__ void write_sorted(Lds<D>& s, const Params& p, int64_t row) {
+__device__ __forceinline__ void write_sorted(Lds<D>& s, const Params& p, int64_t row, uint32_t cnt) {
     constexpr int E = 4;
     uint64_t* buf = reinterpret_cast<uint64_t*>(s.base + p.L.sort);
     const uint32_t k = (uint32_t)p.k;
@@ -1020,24 +1058,37 @@ __device__ __forceinline__ void write_sorted(Lds<D>& s, const Params& p, int64_t
         const uint32_t i0 = threadIdx.x * E;
         uint64_t v[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) v[e] = i0 + e < k ? sort_word<D>(s, i0 + e) : 0ull;
+        for (int e = 0; e < E; ++e) v[e] = i0 + e < cnt ? sort_word<D>(s, i0 + e) : 0ull;
         bitonic_regs<NW, E>(v, n2, buf);
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            if (i0 + e < k) put_sorted<D>(p, row, i0 + e, v[e]);
+            if (i0 + e < k) put_sorted<D>(p, row, i0 + e, v[e], cnt);
     } else {
-        for (uint32_t j = threadIdx.x; j < n2; j += NW * 64) buf[j] = j < k ? sort_word<D>(s, j) : 0ull;
+        for (uint32_t j = threadIdx.x; j < n2; j += NW * 64) buf[j] = j < cnt ? sort_word<D>(s, j) : 0ull;
         bitonic_lds<NW>(buf, n2);
-        for (uint32_t j = threadIdx.x; j < k; j += NW * 64) put_sorted<D>(p, row, j, buf[j]);
+        for (uint32_t j = threadIdx.x; j < k; j += NW * 64) put_sorted<D>(p, row, j, buf[j], cnt);
     }
 }
 
+// Write a row's results: the cnt entries of the candidate buffer (cnt = k
+// unless the row's valid length is below k), then k - cnt fillers.
 template <class D, int NW>
-__device__ __forceinline__ void write_row(Lds<D>& s, const Params& p, int64_t row, uint64_t W, uint64_t A,
-                                          uint64_t R, uint64_t maxlen) {
+__device__ __forceinline__ void write_row(Lds<D>& s, const Params& p, int64_t row, uint32_t cnt, uint64_t W,
+                                          uint64_t A, uint64_t R, uint64_t maxlen) {
     const int64_t k = p.k;
     if (p.sorted) {
-        write_sorted<D, NW>(s, p, row);
+        write_sorted<D, NW>(s, p, row, cnt);
+    } else if (cnt < (uint32_t)k) {
+        for (uint32_t j = threadIdx.x; j < (uint32_t)k; j += NW * 64) {
+            if (j >= cnt) {
+                put_filler<D>(p, row, j);
+            } else if constexpr (is_packed<D>::value) {
+                const uint32_t e = s.keys[j];
+                put_out<D>(p, row, j, D::raw(e >> 16), (int32_t)(e & 0xFFFFu));
+            } else {
+                put_out<D>(p, row, j, D::raw((uint32_t)s.keys[j]), (int32_t)s.idx[j]);
+            }
+        }
     } else if constexpr (is_packed<D>::value) {
         // one part per row: the entry's column is the row's
         for (int64_t j = threadIdx.x; j < k; j += NW * 64) {
@@ -1122,6 +1173,22 @@ __device__ __forceinline__ void write_part(Lds<D>& s, const RunState& st, const 
     }
 }
 
+// Valid length of a row: lengths[row] clamped to [0, n], or n.
+__device__ __forceinline__ int64_t row_len(const Params& p, int64_t row) {
+    if (!p.lengths) return p.n;
+    const int64_t v = p.lengths[row];
+    return v < 0 ? 0 : (v > p.n ? p.n : v);
+}
+
+// Elements of part `part` of a row of n_r valid elements (the parts cut the
+// row's ceil(n_r / B) blocks into S contiguous ranges; some may be empty).
+__device__ __forceinline__ int64_t part_elems(const Params& p, int64_t n_r, int64_t part) {
+    const int64_t m = ceil_div(n_r, (int64_t)p.B);
+    const int64_t e0 = part_begin(m, part, p.split) * (int64_t)p.B;
+    const int64_t e1 = part_begin(m, part + 1, p.split) * (int64_t)p.B;
+    return (e1 < n_r ? e1 : n_r) - (e0 < n_r ? e0 : n_r);
+}
+
 struct PartGeom {
     int64_t row, slot, b0, part_elem0, part_n;
     int32_t part, ms;
@@ -1132,20 +1199,30 @@ __device__ __forceinline__ PartGeom part_geom(const Params& p, int64_t item) {
     g.row = item / p.split;
     g.part = (int32_t)(item % p.split);
     g.slot = item;
-    g.b0 = part_begin(p.m, g.part, p.split);
-    const int64_t b1 = part_begin(p.m, g.part + 1, p.split);
+    const int64_t n_r = row_len(p, g.row);
+    const int64_t m = p.lengths ? ceil_div(n_r, (int64_t)p.B) : p.m;
+    g.b0 = part_begin(m, g.part, p.split);
+    const int64_t b1 = part_begin(m, g.part + 1, p.split);
     g.ms = (int32_t)(b1 - g.b0);
     g.part_elem0 = g.b0 * (int64_t)p.B;
-    g.part_n = ((b1 * (int64_t)p.B < p.n) ? b1 * (int64_t)p.B : p.n) - g.part_elem0;
+    const int64_t e1 = b1 * (int64_t)p.B < n_r ? b1 * (int64_t)p.B : n_r;
+    g.part_n = e1 > g.part_elem0 ? e1 - g.part_elem0 : 0;
     return g;
 }
 
-template <class D>
+// Buffer resource over a part's elements. With kVec the range is rounded up
+// to whole 16-byte loads: a row's valid length need not be a multiple of
+// them, and the 16-byte path only runs on rows whose full length is (so the
+// rounded range stays inside the row); the elements past the part are masked
+// after the load.
+template <class D, bool kVec = true>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const Params& p, const PartGeom& g) {
     const unsigned char* rowp =
         reinterpret_cast<const unsigned char*>(p.x) + (g.row * p.row_stride + g.part_elem0) * D::kBytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(rowp), (short)0,
-                                             (int)(g.part_n * D::kBytes), (int)kRsrcWord3);
+    const int64_t v = kVec ? D::kPerLoad : 1;
+    const int64_t n = (g.part_n + v - 1) / v * v;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(rowp), (short)0, (int)(n * D::kBytes),
+                                             (int)kRsrcWord3);
 }
 
 template <class D, int NW, int U, int Q>
@@ -1172,7 +1249,7 @@ __global__ __launch_bounds__(NW * 64) void deepselect_stream_kernel(Params p) {
         sm.run();
         final_select<D, NW>(s, st, (uint32_t)p.k);
         if (p.split == 1)
-            write_row<D, NW>(s, p, g.row, st.W, st.A, st.R, st.maxlen);
+            write_row<D, NW>(s, p, g.row, st.len, st.W, st.A, st.R, st.maxlen);
         else
             write_part<D, NW>(s, st, p, g.slot, (uint32_t)g.part_elem0);
     }
@@ -1205,7 +1282,7 @@ __global__ __launch_bounds__(NW * 64) void deepselect_ring_kernel(Params p) {
         sm.run();
         final_select<D, NW>(s, st, (uint32_t)p.k);
         if (p.split == 1)
-            write_row<D, NW>(s, p, g.row, st.W, st.A, st.R, st.maxlen);
+            write_row<D, NW>(s, p, g.row, st.len, st.W, st.A, st.R, st.maxlen);
         else
             write_part<D, NW>(s, st, p, g.slot, (uint32_t)g.part_elem0);
     }
@@ -1269,7 +1346,7 @@ __device__ __forceinline__ void load_tile(TileRegs<D, kVec>& r, __amdgpu_buffer_
                                           int32_t tv) {
     constexpr int V = D::kPerLoad;
     if constexpr (kVec) {
-        const bool ok = ((int)threadIdx.x + 1) * V <= tv;
+        const bool ok = (int)threadIdx.x * V < tv;
         const uint32_t off = ok ? (uint32_t)((elem_off + (int64_t)threadIdx.x * V) * D::kBytes) : kOob;
         r.v[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
     } else {
@@ -1412,10 +1489,10 @@ __global__ __launch_bounds__(kGW * 64) void deepselect_generic_kernel(Params p) 
         begin_item<D, kGW>(s);
         build_order<kGW>(s.perm, p.seed, g.row, 0, g.b0, g.ms, s.base);
         RunState st;
-        generic_stream<D, kVec, kVec ? 8 : 4>(s, st, p, part_rsrc<D>(p, g), g.part_elem0, g.part_n, g.ms);
+        generic_stream<D, kVec, kVec ? 8 : 4>(s, st, p, part_rsrc<D, kVec>(p, g), g.part_elem0, g.part_n, g.ms);
         final_select<D, kGW>(s, st, (uint32_t)p.k);
         if (p.split == 1)
-            write_row<D, kGW>(s, p, g.row, st.W, st.A, st.R, st.maxlen);
+            write_row<D, kGW>(s, p, g.row, st.len, st.W, st.A, st.R, st.maxlen);
         else
             write_part<D, kGW>(s, st, p, g.slot, (uint32_t)g.part_elem0);
     }
@@ -1483,12 +1560,14 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
         begin_item<D, NW>(s);
         lds_barrier();
         RunState st;
+        const int64_t n_r = row_len(p, row);
+        bool swap = false;
         if (both) {
             // two parts: the order is (part 1, part 0) exactly when part 1's
             // hash is the smaller (ties go to the lower id), so every thread
             // decides it from the two hashes, with no shared order
             const uint64_t ctr0 = (uint64_t)(row * 2 + 1) << 32;
-            const bool swap = splitmix_at(p.seed, ctr0 + 1u) < splitmix_at(p.seed, ctr0);
+            swap = splitmix_at(p.seed, ctr0 + 1u) < splitmix_at(p.seed, ctr0);
             cur = swap ? pre1 : pre0;
             nxt = swap ? pre0 : pre1;
         } else {
@@ -1498,7 +1577,15 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
         for (int64_t j = 0; j < tiles; ++j) {
             if (!both && j + 1 < tiles) load_merge_tile<NW>(nxt, p, s.perm, row, j + 1, tpp);
             const uint32_t t0 = (uint32_t)(j % tpp) * TE;
-            const uint32_t tv = (k - t0) < TE ? (k - t0) : TE;
+            // results of the part: k, or fewer for a part shorter than k
+            uint32_t cnt = k;
+            if (p.lengths) {
+                const int64_t i = j / tpp;
+                const int64_t part = both ? (swap ? 1 - i : i) : (int64_t)uniform(s.perm[i]);
+                const int64_t e = part_elems(p, n_r, part);
+                cnt = e < (int64_t)k ? (uint32_t)e : k;
+            }
+            const uint32_t tv = t0 < cnt ? ((cnt - t0) < TE ? (cnt - t0) : TE) : 0u;
             uint32_t kmax = 0;
             if (!st.tset) {
 #pragma unroll
@@ -1546,7 +1633,7 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
             R += o[DS_STAT_R];
             maxlen = o[DS_STAT_MAX_LEN] > maxlen ? o[DS_STAT_MAX_LEN] : maxlen;
         }
-        write_row<D, NW>(s, p, row, W, A, R, maxlen);
+        write_row<D, NW>(s, p, row, st.len, W, A, R, maxlen);
     }
 }
 
@@ -1829,6 +1916,7 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     prm.B2 = B2;
     prm.split = (int32_t)S;
     prm.sorted = sorted;
+    prm.lengths = opt ? opt->lengths : nullptr;
     prm.L = L;
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
