@@ -119,6 +119,10 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--sorted", action="store_true",
                     help="results of each row in descending order (ds_options_t.sorted)")
+    ap.add_argument("--sample", action="store_true",
+                    help="fused softmax and one draw per row (sorted output; ds_options_t.probs/sample_u)")
+    ap.add_argument("--temperature", type=float, default=1.0)
+    ap.add_argument("--top-p", type=float, default=1.0)
     ap.add_argument("--lengths", action="store_true",
                     help="pass each row's valid length (ds_options_t.lengths; causal rows end where their "
                          "-inf tail starts, other workloads are full rows)")
@@ -177,8 +181,15 @@ def main() -> int:
         return 1
     lib = ds.library()
     lens = torch.from_numpy(synth.valid_lengths(args.workload)).to(dev) if args.lengths else None
+    if args.sample:
+        args.sorted = True
+        probs = torch.empty((w.batch, w.k), dtype=torch.float32, device=dev)
+        draws = torch.rand(w.batch, generator=torch.Generator().manual_seed(args.seed)).to(dev)
+        sampled = torch.empty(w.batch, dtype=torch.int32, device=dev)
     opt = ds.DsOptions(int(split), int(args.waves), None, None, 0, int(args.kernel), int(args.sorted),
-                       lens.data_ptr() if lens is not None else None)
+                       lens.data_ptr() if lens is not None else None,
+                       probs.data_ptr() if args.sample else None, float(args.temperature), float(args.top_p),
+                       draws.data_ptr() if args.sample else None, sampled.data_ptr() if args.sample else None)
     ptrs = [rot[i].data_ptr() for i in range(copies)]
     vptr, iptr = vals.data_ptr(), idx.data_ptr()
     fn = lib.deepselect_topk_ex
@@ -248,7 +259,7 @@ def main() -> int:
         log(f"[bench] cpu oracle: {cpu}")
 
     # the committed counter figures are for the plain call
-    traffic = None if (args.sorted or args.lengths) else measured_traffic(args.workload)
+    traffic = None if (args.sorted or args.lengths or args.sample) else measured_traffic(args.workload)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -265,6 +276,7 @@ def main() -> int:
         "config": {"workload": args.workload, "batch": w.batch, "N": w.n, "input_dtype": w.dtype,
                    "k": w.k, "B": w.block, "B2": w.block2, "split": int(split), "sorted": bool(args.sorted),
                    "lengths": bool(args.lengths),
+                   "sample": ({"temperature": args.temperature, "top_p": args.top_p} if args.sample else None),
                    "rotating_copies": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -116,6 +116,29 @@ typedef struct ds_options {
      * negative infinity. Statistics count what the prefix costs. The array is
      * read by the kernels; the library does not check it on the host. */
     const int32_t *lengths;
+    /* Fused sampling over each row's results, for the sampling use of the
+     * deep-dive's section "算法设计背景" (top-k over vocabulary logits). Needs
+     * sorted = 1 (DS_ERR_BLOCK otherwise) and k <= 1024 (DS_ERR_UNSUPPORTED).
+     *   probs       device, batch*k floats, or NULL: the softmax of the row's
+     *               results at `temperature` (exp((x_j - max)/temperature)
+     *               over their sum, in float32), in output order; 0 for
+     *               fillers. A row whose largest value is -inf or NaN gets 0.
+     *   temperature > 0 (0 is read as 1).
+     *   top_p       in (0, 1] (0 is read as 1): the sample is drawn from the
+     *               smallest prefix of the sorted results whose probability
+     *               reaches top_p (nucleus sampling).
+     *   sample_u    device, batch floats in [0, 1), or NULL: the draw of each
+     *               row. The sample is the first position of the kept prefix
+     *               whose running sum of exponentials exceeds u times the
+     *               prefix's sum (inverse CDF in descending order).
+     *   sample_idx  device, batch int32, required with sample_u: the sampled
+     *               column (-1 for a row with no finite result).
+     * Values outside these ranges: DS_ERR_BLOCK. */
+    float *probs;
+    float temperature;
+    float top_p;
+    const float *sample_u;
+    int32_t *sample_idx;
 } ds_options_t;
 
 /* Check arguments only (pure host code, no HIP call; usable without a GPU).
@@ -129,7 +152,7 @@ int deepselect_topk(const void *x, int dtype, int64_t batch, int64_t N, int64_t 
                     int32_t *out_idx, void *stream);
 
 /* deepselect_topk with options (forced split, statistics, caller workspace,
- * sorted output, per-row valid lengths).
+ * sorted output, per-row valid lengths, fused sampling).
  * opt may be NULL (then identical to deepselect_topk). */
 int deepselect_topk_ex(const void *x, int dtype, int64_t batch, int64_t N, int64_t row_stride,
                        int32_t k, int32_t B, int32_t B2, uint64_t seed, void *out_vals,

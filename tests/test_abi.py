@@ -65,6 +65,15 @@ def test_topk_ex_rejects_bad_options_before_any_hip_call():
     assert ds.deepselect_topk_ex(*args, kernel=-1) == ds.DS_ERR_BLOCK
     assert ds.deepselect_topk_ex(*args, sorted=2) == ds.DS_ERR_BLOCK
     assert ds.deepselect_topk_ex(*args, sorted=-1) == ds.DS_ERR_BLOCK
+    # fused sampling: sorted output only, a draw needs somewhere to go, the
+    # temperature and top_p in range, k within one register sort
+    assert ds.deepselect_topk_ex(*args, probs=16) == ds.DS_ERR_BLOCK
+    assert ds.deepselect_topk_ex(*args, sorted=1, sample_u=16) == ds.DS_ERR_NULL
+    for t, p in [(-1.0, 1.0), (float("inf"), 1.0), (float("nan"), 1.0), (1.0, 1.5), (1.0, -0.1),
+                 (1.0, float("nan"))]:
+        assert ds.deepselect_topk_ex(*args, sorted=1, probs=16, temperature=t, top_p=p) == ds.DS_ERR_BLOCK
+    big = (16, ds.DS_F32, 2, 4096, 4096, 1025, 256, 256, 0, 16, 16, 0)
+    assert ds.deepselect_topk_ex(*big, sorted=1, probs=16) == ds.DS_ERR_UNSUPPORTED
 
 
 def test_options_struct_matches_the_header(tmp_path):

@@ -18,6 +18,7 @@ import pytest
 import oracle
 import synth
 from oracle import model
+from oracle import sampling as oracle_sampling
 
 torch = pytest.importorskip("torch")
 
@@ -427,3 +428,85 @@ def test_full_lengths_equal_the_plain_call():
     b = run_gpu_len(x, w.k, w.block, w.block2, [w.n] * 8, seed=2, split=2)
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
+
+
+# ---------------------------------------------------------------- fused sampling
+
+def sample_consistent(po: np.ndarray, top_p: float, u: float, s: int, delta: float = 1e-5) -> bool:
+    """Position s is a valid draw for u: the oracle's (float64) cumulative
+    probabilities put u times the nucleus mass between positions s-1 and s, up
+    to delta; near a boundary (of the nucleus or of a position) either side is
+    accepted, since float32 may land on it."""
+    c = np.cumsum(po)
+    jp_o = oracle_sampling.nucleus_end(po, top_p)
+    cands = {jp_o} | {j for j in range(len(po)) if abs(c[j] - top_p) <= delta}
+    for jp in cands:
+        if s > jp:
+            continue
+        target = u * c[jp]
+        lo = c[s - 1] if s > 0 else 0.0
+        if lo <= target + delta and (c[s] >= target - delta or s == jp):
+            return True
+    return False
+
+
+def check_sampling(x, vals, idx, probs, sampled, k, u, temperature, top_p, lengths=None):
+    n = x.shape[1]
+    for r in range(x.shape[0]):
+        L = n if lengths is None else min(max(int(lengths[r]), 0), n)
+        c = min(k, L)
+        po = np.zeros(k)
+        po[:c] = oracle_sampling.softmax(oracle_sampling.values_of(vals[r][:c]), temperature)
+        assert np.all(np.abs(probs[r] - po) <= 2e-5 * po + 1e-9), f"row {r}: probabilities"
+        if c == 0 or po.sum() == 0.0:
+            assert sampled[r] == -1
+            continue
+        pos = np.nonzero(idx[r][:c] == sampled[r])[0]
+        assert len(pos) == 1, f"row {r}: the sampled column is not one of the results"
+        assert sample_consistent(po[:c], top_p, float(u[r]), int(pos[0])), \
+            f"row {r}: draw at position {int(pos[0])} does not fit u={u[r]}"
+
+
+SAMPLE = [
+    # (workload, rows, k or None, temperature, top_p, split)
+    ("vocab152k_k64", 8, None, 1.0, 1.0, 0),
+    ("vocab152k_k64", 8, None, 0.7, 0.9, 0),
+    ("vocab152k_k1024", 4, None, 1.3, 0.95, 0),
+    ("dsa128k_bf16", 4, 1024, 1.0, 0.8, 2),   # bfloat16, the merge kernel writes
+    ("ties1m", 2, None, 1.0, 0.5, 0),         # every result ties: uniform
+    ("gauss4k", 1, 1, 1.0, 1.0, 1),           # k = 1: probability 1
+]
+
+
+@pytest.mark.parametrize("case", SAMPLE, ids=[f"{c[0]}-k{c[2]}-t{c[3]}-p{c[4]}-S{c[5]}" for c in SAMPLE])
+def test_fused_sampling(case):
+    name, rows, k, temperature, top_p, split = case
+    w = synth.WORKLOADS[name]
+    k = w.k if k is None else k
+    log(f"[gpu] fused sampling {case}")
+    x = synth.generate(name, rows)
+    u = np.random.default_rng(11).random(rows, dtype=np.float32)
+    ut = torch.from_numpy(u).to(DEV)
+    v, i, pr, sm = ds.topk_sample(to_device(x), k, w.block, w.block2, ut, seed=6, temperature=temperature,
+                                  top_p=top_p, split=split)
+    torch.cuda.synchronize()
+    vals, idx = raw_of(v), i.cpu().numpy()
+    check_sorted_rows(x, vals, idx, k)
+    check_sampling(x, vals, idx, pr.cpu().numpy(), sm.cpu().numpy(), k, u, temperature, top_p)
+
+
+def test_fused_sampling_short_rows():
+    # rows shorter than k: probabilities over the valid results only, fillers
+    # at 0, and an empty row draws -1
+    n, k, B, B2 = 3000, 64, 256, 128
+    lengths = [0, 1, 40, 64, 65, 3000]
+    x = synth.random_rows(len(lengths), n, "bf16", 17, "gauss")
+    u = np.random.default_rng(3).random(len(lengths), dtype=np.float32)
+    log("[gpu] fused sampling on short rows")
+    lt = torch.from_numpy(np.asarray(lengths, dtype=np.int32)).to(DEV)
+    v, i, pr, sm = ds.topk_sample(to_device(x), k, B, B2, torch.from_numpy(u).to(DEV), seed=1,
+                                  temperature=0.9, top_p=0.97, lengths=lt)
+    torch.cuda.synchronize()
+    vals, idx = raw_of(v), i.cpu().numpy()
+    check_rows_len(x, vals, idx, k, lengths, sorted=True)
+    check_sampling(x, vals, idx, pr.cpu().numpy(), sm.cpu().numpy(), k, u, 0.9, 0.97, lengths)

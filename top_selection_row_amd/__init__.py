@@ -35,7 +35,9 @@ class DsOptions(ctypes.Structure):
     _fields_ = [("split", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("stats", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("kernel", ctypes.c_int32),
-                ("sorted", ctypes.c_int32), ("lengths", ctypes.c_void_p)]
+                ("sorted", ctypes.c_int32), ("lengths", ctypes.c_void_p),
+                ("probs", ctypes.c_void_p), ("temperature", ctypes.c_float), ("top_p", ctypes.c_float),
+                ("sample_u", ctypes.c_void_p), ("sample_idx", ctypes.c_void_p)]
 
 
 _lib = None
@@ -122,9 +124,10 @@ def deepselect_topk(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals, ou
 
 def deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals, out_idx, stream,
                        split=0, stats=None, workspace=None, workspace_bytes=0, waves=0, kernel=0,
-                       sorted=0, lengths=None) -> int:
+                       sorted=0, lengths=None, probs=None, temperature=0.0, top_p=0.0, sample_u=None,
+                       sample_idx=None) -> int:
     opt = DsOptions(int(split), int(waves), stats, workspace, int(workspace_bytes), int(kernel), int(sorted),
-                    lengths)
+                    lengths, probs, float(temperature), float(top_p), sample_u, sample_idx)
     return library().deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed & (2**64 - 1),
                                         out_vals, out_idx, stream, ctypes.byref(opt))
 
@@ -187,3 +190,44 @@ def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, waves: in
     if stats:
         return vals, idx, st
     return vals, idx
+
+
+def topk_sample(x, k: int, B: int, B2: int, u, seed: int = 0, *, temperature: float = 1.0,
+                top_p: float = 1.0, split: int = 0, waves: int = 0, kernel: int = 0, lengths=None,
+                stream=None):
+    """Top-k, softmax and one draw per row, fused into the output of the call.
+
+    ``u``: a float32 device tensor of ``batch`` draws in [0, 1). Returns
+    (vals, idx, probs, sampled): the k results of each row largest first, their
+    softmax at ``temperature`` (float32), and the column drawn by inverse CDF
+    from the smallest prefix whose probability reaches ``top_p`` (int32, -1
+    for a row with no finite result). Needs k <= 1024.
+    """
+    import torch
+
+    if x.dim() != 2 or x.stride(1) != 1 or not x.is_cuda:
+        raise ValueError("x must be a 2-D device tensor with unit stride along the row")
+    if x.dtype == torch.float32:
+        dt = DS_F32
+    elif x.dtype == torch.bfloat16:
+        dt = DS_BF16
+    else:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    batch, n = x.shape
+    if (u.dtype != torch.float32 or u.device != x.device or u.dim() != 1 or u.shape[0] != batch
+            or not u.is_contiguous()):
+        raise ValueError("u must be a contiguous float32 tensor of batch entries on x's device")
+    row_stride = x.stride(0) if batch > 1 else n
+    vals = torch.empty((batch, k), dtype=x.dtype, device=x.device)
+    idx = torch.empty((batch, k), dtype=torch.int32, device=x.device)
+    probs = torch.empty((batch, k), dtype=torch.float32, device=x.device)
+    sampled = torch.empty((batch,), dtype=torch.int32, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        _check(deepselect_topk_ex(x.data_ptr(), dt, batch, n, row_stride, k, B, B2, seed,
+                                  vals.data_ptr(), idx.data_ptr(), stream, split=split, waves=waves,
+                                  kernel=kernel, sorted=1, lengths=_lengths_ptr(lengths, x, batch),
+                                  probs=probs.data_ptr(), temperature=temperature, top_p=top_p,
+                                  sample_u=u.data_ptr(), sample_idx=sampled.data_ptr()))
+    return vals, idx, probs, sampled

@@ -60,6 +60,10 @@ struct Params {
     int32_t k, B, B2, split;
     int32_t sorted;  // write each row's results in descending order
     const int32_t* lengths;  // per-row valid lengths (NULL: every row has n)
+    float* probs;            // softmax of each row's results (sorted output), or NULL
+    const float* sample_u;   // one uniform per row for the sample, or NULL
+    int32_t* sample_idx;     // the sampled column of each row
+    float inv_temp, top_p;
     Layout L;
 };
 
@@ -1047,6 +1051,115 @@ __device__ __forceinline__ void put_sorted(const Params& p, int64_t row, uint32_
         put_filler<D>(p, row, j);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, in float (the same DPP
+// steps as the integer one).
+__device__ __forceinline__ float wave_prefix_sum_f(float v) {
+    v += __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0x111, 0xF, 0xF, true));
+    v += __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0x112, 0xF, 0xF, true));
+    v += __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0x114, 0xF, 0xF, true));
+    v += __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0x118, 0xF, 0xF, true));
+    v += __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0x142, 0xA, 0xF, false));
+    v += __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0x143, 0xC, 0xF, false));
+    return v;
+}
+
+template <class D>
+__device__ __forceinline__ float value_of(uint32_t raw) {
+    return __uint_as_float(D::kBytes == 4 ? raw : raw << 16);
+}
+
+// Fused sampling over a row's cnt results, held sorted as words v (position
+// i0 + e, descending): the softmax of the values at temperature 1/inv_temp
+// (the max-subtracted exponentials over their sum, as in the softmax of
+// "常见CUDA手写实现"), written to probs in output order, and one draw by the
+// inverse of its cumulative distribution in that order: the smallest prefix
+// whose probability reaches top_p is kept, and the sample is the first
+// position whose running sum of exponentials passes u times the prefix's sum.
+// A row whose largest value is -inf or NaN (or that is empty) gets zero
+// probabilities and sample -1. Every wave takes part (workgroup barriers);
+// red is LDS scratch of NW + 4 words.
+template <class D, int NW, int E>
+__device__ __forceinline__ void softmax_sample(const uint64_t (&v)[E], uint32_t i0, uint32_t cnt, const Params& p,
+                                               int64_t row, uint32_t* red) {
+    const uint32_t k = (uint32_t)p.k;
+    const int w = wave_id();
+    uint32_t* r_max = red + NW;
+    uint32_t* r_jp = red + NW + 1;
+    uint32_t* r_cz = red + NW + 2;
+    uint32_t* r_js = red + NW + 3;
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        x[e] = i0 + e < cnt ? value_of<D>(D::raw((uint32_t)(v[e] >> 32))) : -__builtin_huge_valf();
+    if (threadIdx.x == 0) {
+        *r_max = __float_as_uint(x[0]);
+        *r_jp = ~0u;
+        *r_js = ~0u;
+    }
+    lds_barrier();
+    const float m = __uint_as_float(*r_max);
+    const bool live = cnt > 0 && m > -__builtin_huge_valf();  // false for -inf and NaN
+    float ex[E], ts = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        // NaN and -inf results add nothing (-inf > -inf and NaN > -inf are false)
+        ex[e] = live && i0 + e < cnt && x[e] > -__builtin_huge_valf() ? expf((x[e] - m) * p.inv_temp) : 0.f;
+        ts += ex[e];
+    }
+    const float incl = wave_prefix_sum_f(ts);
+    if (lane_id() == 63) red[w] = __float_as_uint(incl);
+    lds_barrier();
+    float before = 0.f, Z = 0.f;  // sums of the waves before this one, and of all
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+        const float t = __uint_as_float(red[q]);
+        before += q < w ? t : 0.f;
+        Z += t;
+    }
+    float c[E];  // running sum of exponentials through each position
+    float run = before + incl - ts;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        run += ex[e];
+        c[e] = run;
+        if (p.probs && i0 + e < k) p.probs[row * k + i0 + e] = live ? ex[e] / Z : 0.f;
+    }
+    if (!p.sample_u) return;
+    // the top-p prefix: positions 0 .. jp
+    uint32_t jp = cnt - 1;
+    float zp = Z;
+    if (p.top_p < 1.f) {
+        const float lim = p.top_p * Z;
+        uint32_t mine = ~0u;
+#pragma unroll
+        for (int e = E - 1; e >= 0; --e)
+            if (i0 + e < cnt && c[e] >= lim) mine = i0 + e;
+        if (mine != ~0u) atomicMin(r_jp, mine);
+        lds_barrier();
+        jp = *r_jp == ~0u ? cnt - 1 : *r_jp;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (i0 + e == jp) *r_cz = __float_as_uint(c[e]);
+        lds_barrier();
+        zp = __uint_as_float(*r_cz);
+    }
+    const float target = p.sample_u[row] * zp;
+    uint32_t mine = ~0u;
+#pragma unroll
+    for (int e = E - 1; e >= 0; --e)
+        if (i0 + e <= jp && i0 + e < cnt && c[e] > target) mine = i0 + e;
+    if (mine != ~0u) atomicMin(r_js, mine);
+    lds_barrier();
+    const uint32_t js = *r_js == ~0u ? jp : *r_js;
+    if (!live) {
+        if (threadIdx.x == 0) p.sample_idx[row] = -1;
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (i0 + e == js) p.sample_idx[row] = (int32_t)~(uint32_t)v[e];
+    }
+}
+
 // Write the row's cnt results in descending order (then k - cnt fillers).
 template <class D, int NW>
 __device__ __forceinline__ void write_sorted(Lds<D>& s, const Params& p, int64_t row, uint32_t cnt) {
@@ -1060,6 +1173,7 @@ __device__ __forceinline__ void write_sorted(Lds<D>& s, const Params& p, int64_t
 #pragma unroll
         for (int e = 0; e < E; ++e) v[e] = i0 + e < cnt ? sort_word<D>(s, i0 + e) : 0ull;
         bitonic_regs<NW, E>(v, n2, buf);
+        if (p.probs || p.sample_u) softmax_sample<D, NW, E>(v, i0, cnt, p, row, s.tot);
 #pragma unroll
         for (int e = 0; e < E; ++e)
             if (i0 + e < k) put_sorted<D>(p, row, i0 + e, v[e], cnt);
@@ -1852,6 +1966,20 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     if (req_kernel < kAuto || req_kernel > kGeneric) return DS_ERR_BLOCK;
     const int sorted = opt ? opt->sorted : 0;
     if (sorted != 0 && sorted != 1) return DS_ERR_BLOCK;
+    // fused sampling: on sorted output, k within one register sort (4 words a
+    // thread of 256)
+    const bool sampling = opt && (opt->probs || opt->sample_u);
+    float inv_temp = 1.f, top_p = 1.f;
+    if (sampling) {
+        if (!sorted) return DS_ERR_BLOCK;
+        if (opt->sample_u && !opt->sample_idx) return DS_ERR_NULL;
+        const float t = opt->temperature == 0.f ? 1.f : opt->temperature;
+        const float tp = opt->top_p == 0.f ? 1.f : opt->top_p;
+        if (!(t > 0.f) || !(t < __builtin_huge_valf()) || !(tp > 0.f && tp <= 1.f)) return DS_ERR_BLOCK;
+        if (k > 1024) return DS_ERR_UNSUPPORTED;
+        inv_temp = 1.f / t;
+        top_p = tp;
+    }
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DS_ERR_HIP;
     DevInfo di;
@@ -1917,6 +2045,11 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     prm.split = (int32_t)S;
     prm.sorted = sorted;
     prm.lengths = opt ? opt->lengths : nullptr;
+    prm.probs = sampling ? opt->probs : nullptr;
+    prm.sample_u = sampling ? opt->sample_u : nullptr;
+    prm.sample_idx = sampling ? opt->sample_idx : nullptr;
+    prm.inv_temp = inv_temp;
+    prm.top_p = top_p;
     prm.L = L;
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
