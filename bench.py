@@ -123,6 +123,8 @@ def main() -> int:
                     help="fused softmax and one draw per row (sorted output; ds_options_t.probs/sample_u)")
     ap.add_argument("--temperature", type=float, default=1.0)
     ap.add_argument("--top-p", type=float, default=1.0)
+    ap.add_argument("--share", action="store_true",
+                    help="split rows share their parts' thresholds (ds_options_t.share_threshold)")
     ap.add_argument("--lengths", action="store_true",
                     help="pass each row's valid length (ds_options_t.lengths; causal rows end where their "
                          "-inf tail starts, other workloads are full rows)")
@@ -189,7 +191,8 @@ def main() -> int:
     opt = ds.DsOptions(int(split), int(args.waves), None, None, 0, int(args.kernel), int(args.sorted),
                        lens.data_ptr() if lens is not None else None,
                        probs.data_ptr() if args.sample else None, float(args.temperature), float(args.top_p),
-                       draws.data_ptr() if args.sample else None, sampled.data_ptr() if args.sample else None)
+                       draws.data_ptr() if args.sample else None, sampled.data_ptr() if args.sample else None,
+                       int(args.share))
     ptrs = [rot[i].data_ptr() for i in range(copies)]
     vptr, iptr = vals.data_ptr(), idx.data_ptr()
     fn = lib.deepselect_topk_ex
@@ -259,7 +262,7 @@ def main() -> int:
         log(f"[bench] cpu oracle: {cpu}")
 
     # the committed counter figures are for the plain call
-    traffic = None if (args.sorted or args.lengths or args.sample) else measured_traffic(args.workload)
+    traffic = None if (args.sorted or args.lengths or args.sample or args.share) else measured_traffic(args.workload)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -275,7 +278,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": w.batch, "N": w.n, "input_dtype": w.dtype,
                    "k": w.k, "B": w.block, "B2": w.block2, "split": int(split), "sorted": bool(args.sorted),
-                   "lengths": bool(args.lengths),
+                   "lengths": bool(args.lengths), "share_threshold": bool(args.share),
                    "sample": ({"temperature": args.temperature, "top_p": args.top_p} if args.sample else None),
                    "rotating_copies": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -139,6 +139,14 @@ typedef struct ds_options {
     float top_p;
     const float *sample_u;
     int32_t *sample_idx;
+    /* Split rows: 1 = the parts of a row share their thresholds (0 = off;
+     * other values DS_ERR_BLOCK). After each compaction a part publishes its
+     * T, and the streaming (ring) kernel filters its next blocks with the
+     * largest T any part of the row has published so far. Any part's k-th
+     * value is at most the row's, so the result set is the same; the
+     * statistics then depend on timing (W = A + k*R still holds per row).
+     * Adds one small kernel (clearing the row cells) before the parts. */
+    int32_t share_threshold;
 } ds_options_t;
 
 /* Check arguments only (pure host code, no HIP call; usable without a GPU).
@@ -152,7 +160,7 @@ int deepselect_topk(const void *x, int dtype, int64_t batch, int64_t N, int64_t 
                     int32_t *out_idx, void *stream);
 
 /* deepselect_topk with options (forced split, statistics, caller workspace,
- * sorted output, per-row valid lengths, fused sampling).
+ * sorted output, per-row valid lengths, fused sampling, shared thresholds).
  * opt may be NULL (then identical to deepselect_topk). */
 int deepselect_topk_ex(const void *x, int dtype, int64_t batch, int64_t N, int64_t row_stride,
                        int32_t k, int32_t B, int32_t B2, uint64_t seed, void *out_vals,

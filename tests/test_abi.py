@@ -65,6 +65,7 @@ def test_topk_ex_rejects_bad_options_before_any_hip_call():
     assert ds.deepselect_topk_ex(*args, kernel=-1) == ds.DS_ERR_BLOCK
     assert ds.deepselect_topk_ex(*args, sorted=2) == ds.DS_ERR_BLOCK
     assert ds.deepselect_topk_ex(*args, sorted=-1) == ds.DS_ERR_BLOCK
+    assert ds.deepselect_topk_ex(*args, share_threshold=2) == ds.DS_ERR_BLOCK
     # fused sampling: sorted output only, a draw needs somewhere to go, the
     # temperature and top_p in range, k within one register sort
     assert ds.deepselect_topk_ex(*args, probs=16) == ds.DS_ERR_BLOCK

@@ -510,3 +510,54 @@ def test_fused_sampling_short_rows():
     vals, idx = raw_of(v), i.cpu().numpy()
     check_rows_len(x, vals, idx, k, lengths, sorted=True)
     check_sampling(x, vals, idx, pr.cpu().numpy(), sm.cpu().numpy(), k, u, 0.9, 0.97, lengths)
+
+
+# ---------------------------------------------------------------- shared thresholds
+
+SHARE = [
+    # (workload, rows, split, sorted, with the causal lengths)
+    ("asc1m", 4, 8, False, False),
+    ("asc1m_b1", 1, 16, True, False),
+    ("ties1m", 4, 8, False, False),
+    ("dsa32k", 8, 4, False, False),
+    ("dsa128k_bf16", 8, 2, False, False),
+    ("dsa128k_bf16", 8, 4, True, True),
+]
+
+
+@pytest.mark.parametrize("case", SHARE, ids=[f"{c[0]}-S{c[2]}-sorted{c[3]}-len{c[4]}" for c in SHARE])
+def test_shared_threshold(case):
+    # the result set is the plain call's; the cost is timing-dependent, but W
+    # = A + k*R holds per row
+    name, rows, split, srt, with_len = case
+    w = synth.WORKLOADS[name]
+    log(f"[gpu] shared thresholds {case}")
+    x = synth.generate(name, rows)
+    xt = to_device(x)
+    kw = dict(split=split, stats=True, sorted=srt)
+    L = None
+    if with_len:
+        L = synth.valid_lengths(name, range(rows))
+        kw["lengths"] = torch.from_numpy(L).to(DEV)
+    plain = ds.topk(xt, w.k, w.block, w.block2, 4, **kw)
+    shared = ds.topk(xt, w.k, w.block, w.block2, 4, share_threshold=True, **kw)
+    torch.cuda.synchronize()
+    vals, idx, st = raw_of(shared[0]), shared[1].cpu().numpy(), shared[2].cpu().numpy()
+    if with_len:
+        check_rows_len(x, vals, idx, w.k, L, sorted=srt)
+    elif srt:
+        check_sorted_rows(x, vals, idx, w.k)
+    else:
+        check_rows(x, vals, idx, w.k)
+    st0 = plain[2].cpu().numpy()
+    assert np.all(st[:, 0] == st[:, 1] + w.k * st[:, 2]), "W = A + k R"
+    log(f"[gpu]   admitted: {int(st0[:, 1].sum())} plain, {int(st[:, 1].sum())} shared")
+    if name.startswith("asc1m"):
+        # ascending rows: the top part's threshold stops the lower parts early
+        assert st[:, 1].sum() <= 0.9 * st0[:, 1].sum(), "sharing did not cut the admissions"
+    # the row cells are cleared by the call itself: a second call gives a
+    # valid result again
+    again = ds.topk(xt, w.k, w.block, w.block2, 4, share_threshold=True, **kw)
+    torch.cuda.synchronize()
+    if not with_len and not srt:
+        check_rows(x, raw_of(again[0]), again[1].cpu().numpy(), w.k)

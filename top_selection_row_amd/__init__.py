@@ -37,7 +37,8 @@ class DsOptions(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t), ("kernel", ctypes.c_int32),
                 ("sorted", ctypes.c_int32), ("lengths", ctypes.c_void_p),
                 ("probs", ctypes.c_void_p), ("temperature", ctypes.c_float), ("top_p", ctypes.c_float),
-                ("sample_u", ctypes.c_void_p), ("sample_idx", ctypes.c_void_p)]
+                ("sample_u", ctypes.c_void_p), ("sample_idx", ctypes.c_void_p),
+                ("share_threshold", ctypes.c_int32)]
 
 
 _lib = None
@@ -125,9 +126,9 @@ def deepselect_topk(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals, ou
 def deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals, out_idx, stream,
                        split=0, stats=None, workspace=None, workspace_bytes=0, waves=0, kernel=0,
                        sorted=0, lengths=None, probs=None, temperature=0.0, top_p=0.0, sample_u=None,
-                       sample_idx=None) -> int:
+                       sample_idx=None, share_threshold=0) -> int:
     opt = DsOptions(int(split), int(waves), stats, workspace, int(workspace_bytes), int(kernel), int(sorted),
-                    lengths, probs, float(temperature), float(top_p), sample_u, sample_idx)
+                    lengths, probs, float(temperature), float(top_p), sample_u, sample_idx, int(share_threshold))
     return library().deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed & (2**64 - 1),
                                         out_vals, out_idx, stream, ctypes.byref(opt))
 
@@ -146,7 +147,8 @@ def _lengths_ptr(lengths, x, batch):
 
 
 def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, waves: int = 0,
-         kernel: int = 0, stats: bool = False, sorted: bool = False, lengths=None, out=None, stream=None):
+         kernel: int = 0, stats: bool = False, sorted: bool = False, lengths=None, share_threshold: bool = False,
+         out=None, stream=None):
     """Row-wise top-k of a 2-D CUDA tensor (float32 or bfloat16, unit column stride).
 
     ``kernel``: 0 library choice, 1 ring streaming, 2 register streaming,
@@ -186,7 +188,8 @@ def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, waves: in
         _check(deepselect_topk_ex(x.data_ptr(), dt, batch, n, row_stride, k, B, B2, seed,
                                   vals.data_ptr(), idx.data_ptr(), stream, split=split, waves=waves,
                                   kernel=kernel, stats=st.data_ptr() if st is not None else None,
-                                  sorted=int(bool(sorted)), lengths=_lengths_ptr(lengths, x, batch)))
+                                  sorted=int(bool(sorted)), lengths=_lengths_ptr(lengths, x, batch),
+                                  share_threshold=int(bool(share_threshold))))
     if stats:
         return vals, idx, st
     return vals, idx

@@ -64,6 +64,8 @@ struct Params {
     const float* sample_u;   // one uniform per row for the sample, or NULL
     int32_t* sample_idx;     // the sampled column of each row
     float inv_temp, top_p;
+    uint64_t* ws_share;      // per row: the largest part threshold key + 1 (0: none), or NULL
+    uint32_t* ws_cnt;        // per part: its number of results (with ws_share)
     Layout L;
 };
 
@@ -75,6 +77,8 @@ struct RunState {
     uint32_t A = 0, R = 0, maxlen = 0;
     uint32_t par = 0;   // count-buffer parity
     uint32_t kmax = 0;  // the largest key this lane appended (reduced over the wave at a select)
+    bool fset = false;  // a threshold filters the blocks (T, or one shared by another part)
+    uint32_t fkey = 0;  // its key: the larger of T and the shared one
 };
 
 template <class D>
@@ -144,6 +148,8 @@ __device__ __forceinline__ void select_buffer(Lds<D>& s, RunState& st, uint32_t 
     st.tkey = select_topk<D, NW>(s.keys, s.idx, s.hist, s.fold, s.tot, s.gathered, s.misc + 2, s.junk, st.len, k, lo,
                                   hi > lo ? hi : lo);
     st.tset = true;
+    st.fkey = st.fset && st.fkey > st.tkey ? st.fkey : st.tkey;
+    st.fset = true;
     st.len = k;
 }
 
@@ -351,10 +357,10 @@ struct Streamer {
         uint32_t c = 0;
         Thresh th{};
         if (mine) {
-            if (!st.tset) {
+            if (!st.fset) {
                 c = blen;
             } else {
-                th = make_thresh<D>(st.tkey);
+                th = make_thresh<D>(st.fkey);
                 c = th.neg ? count_above<true>(r, th.thr) : count_above<false>(r, th.thr);
             }
         }
@@ -378,7 +384,7 @@ struct Streamer {
         const uint32_t run = st.len + uniform(__builtin_amdgcn_readlane(inc, last));
         const uint32_t my_base = st.len + uniform(__builtin_amdgcn_readlane(inc - cg, w));
         if (mine && w <= last && c != 0) {
-            if (!st.tset)
+            if (!st.fset)
                 scatter_all(r, my_base, boff, blen);
             else if (th.neg)
                 scatter_above<true>(r, my_base, boff, th.thr);
@@ -468,6 +474,7 @@ struct RingStreamer {
     const int32_t ms, nsteps, depth;
     const uint32_t k, B2;
     u32x4* ring;  // this wave's slots: slot q unit u at ring[(q*U + u)*64 + lane]
+    uint64_t* share;  // the row's shared threshold cell (key + 1, 0: none), or NULL
 
     __device__ __forceinline__ void block_at(int32_t bi, uint32_t& boff, uint32_t& blen) const {
         if (bi >= ms) {
@@ -761,10 +768,10 @@ struct RingStreamer {
         uint32_t lc = 0, lm = 0;
         Thresh th{};
         if (mine) {
-            if (!st.tset) {
+            if (!st.fset) {
                 lc = lane_valid(blen);
             } else {
-                th = make_thresh<D>(st.tkey);
+                th = make_thresh<D>(st.fkey);
                 lm = th.neg ? lane_mask<true>(r, th.thr) : lane_mask<false>(r, th.thr);
                 lc = mask_count(lm);
             }
@@ -792,7 +799,7 @@ struct RingStreamer {
         const uint32_t my_base = st.len + uniform(__builtin_amdgcn_readlane(inc - cg, w));
         if (mine && w <= last && c != 0) {
             const uint32_t pos = my_base + incl - lc;
-            if (!st.tset) {
+            if (!st.fset) {
                 if (blen == (uint32_t)(U * UE) && (my_base & 7u) == 0u)
                     append_full(r, my_base, boff);
                 else
@@ -838,6 +845,7 @@ struct RingStreamer {
         int32_t issued = 0;  // steps whose block of this wave is fetched
         if (nsteps > 0) fetch(w, 0), issued = 1;
         BlockRegs<U> r;
+        uint64_t shared = 0;  // the row's shared threshold cell, as read before the last refill
         for (int32_t stp = 0; stp < nsteps; ++stp) {
             const int32_t q = stp % depth;
             const int32_t nblk = ms - stp * NW < NW ? ms - stp * NW : NW;  // blocks in this step
@@ -845,6 +853,12 @@ struct RingStreamer {
             block_at(stp * NW + w, boff, blen);
             wait_block(issued - 1 - stp);
             read_slot(q, r);
+            if (share && shared != 0u) {
+                // another part's threshold (any part's k-th is at most the
+                // row's) raises the filter of this wave's next blocks
+                const uint32_t key = uniform((uint32_t)(shared - 1u));
+                if (!st.fset || key > st.fkey) st.fkey = key, st.fset = true;
+            }
             if (stp == 0) {
                 for (; issued < depth && issued < nsteps; ++issued) fetch(issued * NW + w, issued);
             }
@@ -854,11 +868,16 @@ struct RingStreamer {
                 const int32_t trig = append_from(r, boff, blen, first, nblk, ring + q * U * 64);
                 if (trig < 0) break;
                 compact<D, NW>(s, st, k);
+                if (share && threadIdx.x == 0)
+                    __hip_atomic_fetch_max(share, (uint64_t)st.tkey + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (trig >= nblk - 1) break;
                 first = trig + 1;  // the blocks behind it, against the new T
             }
             if (issued < nsteps) {
                 wait_lgkm();  // this wave's reads of slot q are done before it is refilled
+                // read before the refill, so the next step's wait for its
+                // block covers it
+                if (share) shared = __hip_atomic_load(share, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 fetch(issued * NW + w, q);
                 ++issued;
             }
@@ -1254,6 +1273,9 @@ __device__ __forceinline__ void write_row(Lds<D>& s, const Params& p, int64_t ro
 template <class D, int NW>
 __device__ __forceinline__ void write_part(Lds<D>& s, const RunState& st, const Params& p, int64_t slot,
                                            uint32_t part_elem0) {
+    // the part's number of results: k, or fewer for a short part or one
+    // filtered by a shared threshold
+    if (p.ws_cnt && threadIdx.x == 0) p.ws_cnt[slot] = st.len;
     if constexpr (is_packed<D>::value) {
         for (int64_t j = threadIdx.x; j < p.k; j += NW * 64) {
             const uint32_t e = s.keys[j];
@@ -1292,15 +1314,6 @@ __device__ __forceinline__ int64_t row_len(const Params& p, int64_t row) {
     if (!p.lengths) return p.n;
     const int64_t v = p.lengths[row];
     return v < 0 ? 0 : (v > p.n ? p.n : v);
-}
-
-// Elements of part `part` of a row of n_r valid elements (the parts cut the
-// row's ceil(n_r / B) blocks into S contiguous ranges; some may be empty).
-__device__ __forceinline__ int64_t part_elems(const Params& p, int64_t n_r, int64_t part) {
-    const int64_t m = ceil_div(n_r, (int64_t)p.B);
-    const int64_t e0 = part_begin(m, part, p.split) * (int64_t)p.B;
-    const int64_t e1 = part_begin(m, part + 1, p.split) * (int64_t)p.B;
-    return (e1 < n_r ? e1 : n_r) - (e0 < n_r ? e0 : n_r);
 }
 
 struct PartGeom {
@@ -1392,7 +1405,8 @@ __global__ __launch_bounds__(NW * 64) void deepselect_ring_kernel(Params p) {
                                   p.L.ring_depth,
                                   (uint32_t)p.k,
                                   (uint32_t)p.B2,
-                                  ring};
+                                  ring,
+                                  p.ws_share ? p.ws_share + g.row : nullptr};
         sm.run();
         final_select<D, NW>(s, st, (uint32_t)p.k);
         if (p.split == 1)
@@ -1505,7 +1519,7 @@ __device__ __forceinline__ void generic_tile(Lds<D>& s, RunState& st, const Tile
     constexpr int V = D::kPerLoad;
     if (tv <= 0) return;
     uint32_t kmax = 0;
-    if (!st.tset) {
+    if (!st.fset) {
 #pragma unroll
         for (int q = 0; q < V; ++q) {
             const int e = tile_elem<D, kVec>(q);
@@ -1521,7 +1535,7 @@ __device__ __forceinline__ void generic_tile(Lds<D>& s, RunState& st, const Tile
         st.A += (uint32_t)tv;
         return;
     }
-    const Thresh th = make_thresh<D>(st.tkey);
+    const Thresh th = make_thresh<D>(st.fkey);
     bool pred[V];
     uint64_t masks[V];
 #pragma unroll
@@ -1669,12 +1683,17 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
             load_part_tile<NW>(pre0, p, row, 0, 0);
             load_part_tile<NW>(pre1, p, row, 1, 0);
         }
+        // the parts' result counts (short or filtered parts), lane q holding
+        // part q's, loaded with the first tiles (more than 64 parts: read
+        // where needed)
+        const bool counted = p.lengths || p.ws_share;
+        uint32_t part_cnt = k;
+        if (counted && S <= 64 && lane_id() < S) part_cnt = p.ws_cnt[row * S + lane_id()];
         // the previous row's final select has ended, so the histogram and the
         // largest-key cell are free to clear before the barrier that frees LDS
         begin_item<D, NW>(s);
         lds_barrier();
         RunState st;
-        const int64_t n_r = row_len(p, row);
         bool swap = false;
         if (both) {
             // two parts: the order is (part 1, part 0) exactly when part 1's
@@ -1691,13 +1710,14 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
         for (int64_t j = 0; j < tiles; ++j) {
             if (!both && j + 1 < tiles) load_merge_tile<NW>(nxt, p, s.perm, row, j + 1, tpp);
             const uint32_t t0 = (uint32_t)(j % tpp) * TE;
-            // results of the part: k, or fewer for a part shorter than k
+            // results of the part: k, or fewer for a part shorter than k or
+            // one filtered by a shared threshold
             uint32_t cnt = k;
-            if (p.lengths) {
+            if (counted) {
                 const int64_t i = j / tpp;
                 const int64_t part = both ? (swap ? 1 - i : i) : (int64_t)uniform(s.perm[i]);
-                const int64_t e = part_elems(p, n_r, part);
-                cnt = e < (int64_t)k ? (uint32_t)e : k;
+                cnt = S <= 64 ? uniform(__builtin_amdgcn_readlane(part_cnt, (int)part))
+                              : uniform(p.ws_cnt[row * S + part]);
             }
             const uint32_t tv = t0 < cnt ? ((cnt - t0) < TE ? (cnt - t0) : TE) : 0u;
             uint32_t kmax = 0;
@@ -1749,6 +1769,13 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
         }
         write_row<D, NW>(s, p, row, st.len, W, A, R, maxlen);
     }
+}
+
+// Clear n 64-bit words (the rows' shared threshold cells, before the parts
+// start): a kernel, not a memset, so that the call stays capturable.
+__global__ void deepselect_zero_kernel(uint64_t* p, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
 }
 
 // ===========================================================================
@@ -1968,6 +1995,8 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     if (req_kernel < kAuto || req_kernel > kGeneric) return DS_ERR_BLOCK;
     const int sorted = opt ? opt->sorted : 0;
     if (sorted != 0 && sorted != 1) return DS_ERR_BLOCK;
+    const int share = opt ? opt->share_threshold : 0;
+    if (share != 0 && share != 1) return DS_ERR_BLOCK;
     // fused sampling: on sorted output, k within one register sort (4 words a
     // thread of 256)
     const bool sampling = opt && (opt->probs || opt->sample_u);
@@ -2068,8 +2097,15 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
         prm.ws_keys = reinterpret_cast<uint32_t*>(w + wl.keys);
         prm.ws_idx = reinterpret_cast<uint32_t*>(w + wl.idx);
         prm.ws_stats = reinterpret_cast<uint64_t*>(w + wl.stats);
+        prm.ws_cnt = reinterpret_cast<uint32_t*>(w + wl.cnt);
+        prm.ws_share = share ? reinterpret_cast<uint64_t*>(w + wl.share) : nullptr;
     }
     const int64_t items = batch * S;
+    if (prm.ws_share) {
+        const int64_t blocks = std::min<int64_t>(ceil_div(batch, 256), 1024);
+        hipLaunchKernelGGL(deepselect_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, hs, prm.ws_share, batch);
+        if (hipGetLastError() != hipSuccess) return DS_ERR_HIP;
+    }
     if (dtype == DS_F32) return launch_all<F32T, F32T>(kind, units, waves, vec, prm, hs, items);
     if (packed) return launch_all<BF16P, BF16T>(kind, units, waves, vec, prm, hs, items);
     return launch_all<BF16T, BF16T>(kind, units, waves, vec, prm, hs, items);

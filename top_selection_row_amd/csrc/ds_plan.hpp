@@ -165,7 +165,7 @@ inline Layout make_merge_layout(int dtype, int64_t k, int64_t B2, int64_t S, int
 // Workspace of split rows (device memory): every part's k (key, column) pairs
 // and its four statistics. The merge kernel reads it after the part kernel.
 struct WsLayout {
-    size_t keys, idx, stats, total;
+    size_t keys, idx, stats, cnt, share, total;
 };
 
 inline WsLayout make_ws_layout(int64_t batch, int64_t k, int64_t S) {
@@ -178,6 +178,10 @@ inline WsLayout make_ws_layout(int64_t batch, int64_t k, int64_t S) {
     off = align_up(off + (size_t)batch * S * k * 4, 256);
     w.stats = off;
     off = align_up(off + (size_t)batch * S * 4 * 8, 256);
+    w.cnt = off;  // each part's number of results (uint32)
+    off = align_up(off + (size_t)batch * S * 4, 256);
+    w.share = off;  // each row's shared threshold key + 1 (uint64, zero between calls)
+    off = align_up(off + (size_t)batch * 8, 256);
     w.total = off;
     return w;
 }
