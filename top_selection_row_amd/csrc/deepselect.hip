@@ -65,7 +65,8 @@ struct Params {
     int32_t* sample_idx;     // the sampled column of each row
     float inv_temp, top_p;
     uint64_t* ws_share;      // per row: the largest part threshold key + 1 (0: none), or NULL
-    uint32_t* ws_cnt;        // per part: its number of results (with ws_share)
+    uint32_t* ws_cnt;        // per part: its number of results
+    uint32_t* ws_tkey;       // per part: its k-th key when it has k results, else 0
     Layout L;
 };
 
@@ -79,6 +80,7 @@ struct RunState {
     uint32_t kmax = 0;  // the largest key this lane appended (reduced over the wave at a select)
     bool fset = false;  // a threshold filters the blocks (T, or one shared by another part)
     uint32_t fkey = 0;  // its key: the larger of T and the shared one
+    uint32_t lo0 = 0;   // before T is set: a key the row's k-th is known to reach (0: none)
 };
 
 template <class D>
@@ -134,7 +136,7 @@ __device__ __forceinline__ void publish_max(RunState& st, uint32_t kmax) {
 template <class D, int NW>
 __device__ __forceinline__ void select_buffer(Lds<D>& s, RunState& st, uint32_t k) {
     static_assert(NW <= 8, "one largest-key cell per wave in misc[8..16)");
-    const uint32_t lo = st.tset ? st.tkey : 0u;
+    const uint32_t lo = st.tset ? st.tkey : st.lo0;
     const uint32_t wmax = wave_max(st.kmax);
     if (lane_id() == 0) s.misc[8 + wave_id()] = wmax;
     lds_barrier();  // appends and the waves' largest keys are visible
@@ -146,7 +148,7 @@ __device__ __forceinline__ void select_buffer(Lds<D>& s, RunState& st, uint32_t 
     }
     hi = uniform(hi);
     st.tkey = select_topk<D, NW>(s.keys, s.idx, s.hist, s.fold, s.tot, s.gathered, s.misc + 2, s.junk, st.len, k, lo,
-                                  hi > lo ? hi : lo);
+                                  hi > lo ? hi : lo, st.tset || lo == 0u);
     st.tset = true;
     st.fkey = st.fset && st.fkey > st.tkey ? st.fkey : st.tkey;
     st.fset = true;
@@ -1275,7 +1277,10 @@ __device__ __forceinline__ void write_part(Lds<D>& s, const RunState& st, const 
                                            uint32_t part_elem0) {
     // the part's number of results: k, or fewer for a short part or one
     // filtered by a shared threshold
-    if (p.ws_cnt && threadIdx.x == 0) p.ws_cnt[slot] = st.len;
+    if (p.ws_cnt && threadIdx.x == 0) {
+        p.ws_cnt[slot] = st.len;
+        p.ws_tkey[slot] = st.len == (uint32_t)p.k && st.tset ? st.tkey : 0u;
+    }
     if constexpr (is_packed<D>::value) {
         for (int64_t j = threadIdx.x; j < p.k; j += NW * 64) {
             const uint32_t e = s.keys[j];
@@ -1687,14 +1692,16 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
         // part q's, loaded with the first tiles (more than 64 parts: read
         // where needed)
         const bool counted = p.lengths || p.ws_share;
-        uint32_t part_cnt = k;
+        uint32_t part_cnt = k, part_t = 0;
         if (counted && S <= 64 && lane_id() < S) part_cnt = p.ws_cnt[row * S + lane_id()];
+        if (S <= 64 && lane_id() < S) part_t = p.ws_tkey[row * S + lane_id()];
         // the previous row's final select has ended, so the histogram and the
         // largest-key cell are free to clear before the barrier that frees LDS
         begin_item<D, NW>(s);
         lds_barrier();
         RunState st;
         bool swap = false;
+
         if (both) {
             // two parts: the order is (part 1, part 0) exactly when part 1's
             // hash is the smaller (ties go to the lower id), so every thread
@@ -1753,6 +1760,15 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
             }
             publish_max(st, kmax);
             if ((j + 1) % tpp == 0) {  // a part's block ends: the compaction check
+                // an appended part's k-th key is at most the buffer's k-th
+                // from now on: the largest so far bounds the merge's select
+                // from below (a part with fewer than k results gives none)
+                if (S <= 64) {
+                    const int64_t i = j / tpp;
+                    const int64_t part = both ? (swap ? 1 - i : i) : (int64_t)uniform(s.perm[i]);
+                    const uint32_t t = uniform(__builtin_amdgcn_readlane(part_t, (int)part));
+                    st.lo0 = t > st.lo0 ? t : st.lo0;
+                }
                 st.maxlen = st.len > st.maxlen ? st.len : st.maxlen;
                 if (st.len >= k + B2) compact<D, NW>(s, st, k);
             }
@@ -2098,6 +2114,7 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
         prm.ws_idx = reinterpret_cast<uint32_t*>(w + wl.idx);
         prm.ws_stats = reinterpret_cast<uint64_t*>(w + wl.stats);
         prm.ws_cnt = reinterpret_cast<uint32_t*>(w + wl.cnt);
+        prm.ws_tkey = reinterpret_cast<uint32_t*>(w + wl.tkey);
         prm.ws_share = share ? reinterpret_cast<uint64_t*>(w + wl.share) : nullptr;
     }
     const int64_t items = batch * S;

@@ -577,12 +577,12 @@ __device__ __forceinline__ uint32_t finish_gathered(const typename D::Key* keys,
 template <class D, int NW>
 __device__ uint32_t select_topk(typename D::Key* keys, uint32_t* idx, uint32_t* hist, uint32_t* folded,
                                 uint32_t* tot, uint32_t* gathered, uint32_t* gcount, uint32_t junk, uint32_t n,
-                                uint32_t k, uint32_t lo, uint32_t hi) {
+                                uint32_t k, uint32_t lo, uint32_t hi, bool all_in = true) {
     lds_barrier();
     uint32_t base = lo, span = hi - lo, rank = k;
     int s = span ? 32 - __clz(span) : 0;  // bit length of the span
     s = s > 8 ? s - 8 : 0;
-    bool first = true;  // the first pass's window holds every key
+    bool first = all_in;  // the first pass's window holds every key
     while (true) {
         if (first)
             hist_pass<D, NW, true>(keys, n, base, span, s, hist);

@@ -165,7 +165,7 @@ inline Layout make_merge_layout(int dtype, int64_t k, int64_t B2, int64_t S, int
 // Workspace of split rows (device memory): every part's k (key, column) pairs
 // and its four statistics. The merge kernel reads it after the part kernel.
 struct WsLayout {
-    size_t keys, idx, stats, cnt, share, total;
+    size_t keys, idx, stats, cnt, tkey, share, total;
 };
 
 inline WsLayout make_ws_layout(int64_t batch, int64_t k, int64_t S) {
@@ -179,6 +179,8 @@ inline WsLayout make_ws_layout(int64_t batch, int64_t k, int64_t S) {
     w.stats = off;
     off = align_up(off + (size_t)batch * S * 4 * 8, 256);
     w.cnt = off;  // each part's number of results (uint32)
+    off = align_up(off + (size_t)batch * S * 4, 256);
+    w.tkey = off;  // each part's k-th key when it has k results, else 0 (uint32)
     off = align_up(off + (size_t)batch * S * 4, 256);
     w.share = off;  // each row's shared threshold key + 1 (uint64, zero between calls)
     off = align_up(off + (size_t)batch * 8, 256);
