@@ -10,26 +10,33 @@
 //
 // Mapping on gfx950
 //   * one workgroup per (row, part) owns the candidate buffer (keys + column
-//     indices), the radix histograms and the block order in LDS;
-//   * streaming kernel: each wave owns whole blocks. A step hands the next NW
-//     blocks of the order to the NW waves; each lane holds its share of its
-//     block in registers (U 16-byte buffer loads) while the wave counts the
-//     elements above T with 64-bit ballots. One barrier exchanges the NW counts,
-//     after which every wave knows where its survivors go and whether some
-//     block of the step ends with the buffer at k + B2 or more. If so, the
-//     buffer is compacted right after that block and the later blocks of the
-//     step are counted again against the new T, so the result and every
-//     statistic are those of the block-by-block loop of the pages. Loads run P
-//     steps ahead of use; lanes past the end of a block get an out-of-range
-//     buffer offset, which returns zero and touches no memory;
+//     indices, or packed key/column words for bfloat16 parts of at most 64K
+//     elements), the radix histograms and the block order in LDS;
+//   * ring kernel (the usual path): each wave owns whole blocks. A step hands
+//     the next NW blocks of the order to the NW waves; blocks travel HBM ->
+//     LDS with buffer loads that write LDS directly, into a ring of slots per
+//     wave, and a step waits only for its own block. Each wave counts its
+//     elements above T; one barrier exchanges the NW counts, after which every
+//     wave knows where its survivors go and whether some block of the step
+//     ends with the buffer at k + B2 or more. If so, the buffer is compacted
+//     right after that block and the later blocks of the step are counted
+//     again against the new T, so the result and every statistic are those of
+//     the block-by-block loop of the pages;
+//   * register-streaming kernel: the same step loop with blocks held in
+//     registers, Q steps of loads in flight (when the ring does not fit LDS);
 //   * generic kernel (unaligned rows, ragged N, blocks over 8 KiB): the whole
 //     workgroup shares each block, one barrier per 4 KiB tile;
 //   * split rows (the deep-dive's "实现" section, last paragraph: a row cut into
-//     parts whose top-k go to one reducer): each part writes its k results to a
-//     device workspace; a second kernel, queued behind the first on the same
-//     stream, runs DeepSelect over the parts' results (one block per part) and
-//     writes the row. The kernel boundary makes the parts' writes visible, so
-//     no device-wide fence or arrival counter is needed.
+//     parts whose top-k go to one reducer): each part writes its results, their
+//     count and its k-th key to a device workspace; a second kernel, queued
+//     behind the first on the same stream, runs DeepSelect over the parts'
+//     results (one block per part) and writes the row. The kernel boundary
+//     makes the parts' writes visible, so no device-wide fence or arrival
+//     counter is needed;
+//   * the kernel that writes a row can sort its results (a bitonic network in
+//     registers and LDS), take a softmax and draw a sample from them; rows may
+//     have their own valid lengths; the parts of a split row may share their
+//     thresholds (a device-scope atomic maximum per row).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
