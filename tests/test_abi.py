@@ -152,3 +152,17 @@ def test_workspace_layout():
 def test_workspace_zero_without_split():
     assert ds.deepselect_workspace_bytes(ds.DS_F32, 8, 1000, 10, 100, 100, 1) == 0
     assert ds.deepselect_workspace_bytes(ds.DS_F32, 8, 1000, 0, 100, 100, 2) == 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # one GPU is measured; a request for more exits with a message before any
+    # device work
+    import pathlib
+    import subprocess
+    import sys
+
+    root = pathlib.Path(__file__).resolve().parents[1]
+    r = subprocess.run([sys.executable, str(root / "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
