@@ -86,8 +86,10 @@ typedef struct ds_options {
     uint64_t *stats;
     /* Device workspace for split rows, or NULL for the library-owned one.
      * Size from deepselect_workspace_bytes; no initial contents are needed. It
-     * holds every part's k candidates between the part kernel and the merge
-     * kernel, so it must not be shared by calls that may overlap. */
+     * holds every part's results (up to k), their count, the part's k-th key
+     * and statistics between the part kernel and the merge kernel, and the
+     * rows' shared-threshold cells, so it must not be shared by calls that may
+     * overlap. */
     void *workspace;
     size_t workspace_bytes;
     /* Kernel: 0 = library choice; 1 = ring streaming (blocks copied HBM -> LDS
