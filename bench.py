@@ -78,10 +78,32 @@ def cpu_baseline(workload: str, seconds: float):
         if el >= seconds:
             break
     gelem = done * rows * w.n / el / 1e9
+    # the same oracle on one thread, over 8 rows for a third of the time
+    rows1 = min(rows, 8)
+    done1, t0 = 0, time.perf_counter()
+    while True:
+        oracle.topk(x[:rows1], w.k, nthreads=1)
+        done1 += 1
+        el1 = time.perf_counter() - t0
+        if el1 >= seconds / 3:
+            break
     del np
     return {"value": round(gelem, 4), "unit": "Gelem/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} passes of the oracle (C full sort) over {rows} of the {w.batch} "
-                      f"rows, {el:.1f} s"}
+                      f"rows, {el:.1f} s",
+            "one_thread": round(done1 * rows1 * w.n / el1 / 1e9, 4),
+            "host": f"{host_cpu()}, {os.cpu_count()} logical CPUs"}
+
+
+def host_cpu() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def copy_calibration(args, torch) -> int:

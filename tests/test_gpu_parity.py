@@ -221,6 +221,57 @@ def test_edge_shapes(case):
     check_rows(x, vals, idx, k)
 
 
+# The largest rows the library takes: N = 2^31 - 1 bfloat16 (one 4 GiB row) and
+# two float32 rows of 2^29 + 4 elements (the second starts past byte 2^31).
+# The background is a repeating run of negative values, and k distinct positive
+# values are planted at seeded positions (both ends of the row among them), so
+# by the plain definition the top k are exactly the planted entries, in the
+# order of their values: a closed form the oracle's full sort would take
+# minutes to reproduce at this size.
+MAXROW = [("bf16", 1, (1 << 31) - 1, 2048, 2048, 2048, True),
+          ("f32", 2, (1 << 29) + 4, 512, 1024, 1024, False)]
+
+
+@pytest.mark.parametrize("case", MAXROW, ids=[f"{c[0]}-{c[1]}x{c[2]}" for c in MAXROW])
+def test_maximum_row_length(case):
+    dt, batch, n, k, B, B2, srt = case
+    log(f"[gpu] maximum rows {case}")
+    rng = np.random.default_rng(2024)
+    tdt = torch.int16 if dt == "bf16" else torch.int32
+    x = torch.empty((batch, n), dtype=tdt, device=DEV)
+    step = 1 << 27
+    for a in range(0, n, step):
+        b = min(n, a + step)
+        j = torch.arange(a, b, device=DEV, dtype=torch.int64) % 251
+        if dt == "bf16":  # -1.0 (0xBF80) and the 250 bfloat16 values below it
+            x[:, a:b] = (j + (0xBF80 - 65536)).to(torch.int16)
+        else:  # -1 ... -251
+            x[:, a:b] = (-(j + 1)).to(torch.float32).view(torch.int32)
+    pos = np.empty((batch, k), dtype=np.int64)
+    planted = np.empty((batch, k), dtype=np.int64)
+    for r in range(batch):
+        p = rng.choice(n - 2, size=k - 2, replace=False) + 1
+        pos[r] = rng.permutation(np.concatenate([[0, n - 1], p]))
+        if dt == "bf16":  # 1.0 (0x3F80) and the next k - 1 bfloat16 values
+            planted[r] = 0x3F80 + rng.permutation(k)
+        else:  # 1.0 ... k
+            planted[r] = np.arange(1, k + 1, dtype=np.float32)[rng.permutation(k)].view(np.int32)
+        x[r, torch.from_numpy(pos[r]).to(DEV)] = torch.from_numpy(planted[r]).to(DEV).to(tdt)
+    xt = x.view(torch.bfloat16) if dt == "bf16" else x.view(torch.float32)
+    vals, idx = ds.topk(xt, k, B, B2, sorted=srt)
+    torch.cuda.synchronize()
+    del x, xt
+    got_v = raw_of(vals).astype(np.int64)
+    got_i = idx.cpu().numpy().astype(np.int64)
+    bits = 0xFFFF if dt == "bf16" else 0xFFFFFFFF
+    for r in range(batch):
+        want = dict(zip(pos[r].tolist(), (planted[r] & bits).tolist()))
+        assert sorted(got_i[r].tolist()) == sorted(want), f"row {r}: index set differs from the planted one"
+        assert [want[i] for i in got_i[r].tolist()] == got_v[r].tolist(), f"row {r}: value bits differ"
+        if srt:  # the planted values are positive, so larger bits are larger values
+            assert np.all(np.diff(got_v[r]) < 0), f"row {r}: not in descending order"
+
+
 @pytest.mark.parametrize("dt,k,split", [("bf16", 301, 3), ("f32", 77, 2), ("f32", 1, 5), ("bf16", 2, 4)])
 def test_split_odd_k(dt, k, split):
     # k not a multiple of 4: the parts' results and the merged row are written
