@@ -612,3 +612,58 @@ def test_shared_threshold(case):
     torch.cuda.synchronize()
     if not with_len and not srt:
         check_rows(x, raw_of(again[0]), again[1].cpu().numpy(), w.k)
+
+
+# ---------------------------------------------------------------- randomised parity
+
+def draw_case(i):
+    """Seeded draw of one call: dtype, shape, values, k, B, B2, split, waves,
+    kernel, sorted output and valid lengths (redrawn until the library takes
+    the shape and the method model stays quick)."""
+    rng = np.random.default_rng(7000 + i)
+    while True:
+        dt = str(rng.choice(["f32", "bf16"]))
+        batch = int(rng.integers(1, 7))
+        n = max(1, int(np.exp(rng.uniform(0.0, np.log(40000.0)))))
+        k = max(1, int(np.exp(rng.uniform(0.0, np.log(min(n, 2500))))))
+        B = max(1, int(np.exp(rng.uniform(0.0, np.log(4096.0)))))
+        B2 = max(1, int(np.exp(rng.uniform(0.0, np.log(4096.0)))))
+        dcode = ds.DS_F32 if dt == "f32" else ds.DS_BF16
+        if ds.deepselect_validate(dcode, batch, n, n, k, B, B2) != 0 or -(-n // B) > 3000:
+            continue
+        lengths = rng.integers(-2, n + 3, batch) if rng.random() < 0.3 else None
+        return dict(dt=dt, batch=batch, n=n, k=k, B=B, B2=B2, kind=str(rng.choice(["gauss", "small_ints", "special"])),
+                    split=int(rng.choice([0, 0, 1, 2, 3, 5])), waves=int(rng.choice([0, 4, 8])),
+                    kernel=int(rng.choice([0, 0, 1, 2, 3])), sorted=bool(rng.integers(2)), lengths=lengths,
+                    seed=int(rng.integers(0, 2**63, dtype=np.uint64)), data=int(rng.integers(1 << 30)))
+
+
+@pytest.mark.parametrize("i", range(150))
+def test_random_calls(i):
+    c = draw_case(i)
+    log(f"[gpu] random call {i}: " + ", ".join(f"{a}={c[a]}" for a in ("dt", "batch", "n", "k", "B", "B2", "kind",
+                                                                        "split", "waves", "kernel", "sorted")))
+    x = synth.random_rows(c["batch"], c["n"], c["dt"], c["data"], c["kind"])
+    xt = to_device(x)
+    lt = None if c["lengths"] is None else torch.from_numpy(c["lengths"].astype(np.int32)).to(DEV)
+    split, waves, kernel = c["split"], c["waves"], c["kernel"]
+    try:
+        out = ds.topk(xt, c["k"], c["B"], c["B2"], c["seed"], split=split, stats=True, waves=waves, kernel=kernel,
+                      sorted=c["sorted"], lengths=lt)
+    except ds.DeepSelectArgumentError:
+        # a forced split, wave count or kernel this shape does not allow: the
+        # library's own choice must take it
+        assert (split, waves, kernel) != (0, 0, 0)
+        log(f"[gpu]   split={split} waves={waves} kernel={kernel} refused for this shape; library choice")
+        split, waves, kernel = 0, 0, 0
+        out = ds.topk(xt, c["k"], c["B"], c["B2"], c["seed"], stats=True, sorted=c["sorted"], lengths=lt)
+    torch.cuda.synchronize()
+    vals, idx, st = raw_of(out[0]), out[1].cpu().numpy(), out[2].cpu().numpy()
+    n, k = c["n"], c["k"]
+    lengths = c["lengths"] if c["lengths"] is not None else np.full(c["batch"], n)
+    check_rows_len(x, vals, idx, k, lengths, sorted=c["sorted"])
+    if split == 0:
+        dcode = ds.DS_F32 if c["dt"] == "f32" else ds.DS_BF16
+        split = ds.deepselect_plan_split(dcode, c["batch"], n, k, c["B"], c["B2"],
+                                         torch.cuda.get_device_properties(0).multi_processor_count)
+    check_stats_len(x, st, k, c["B"], c["B2"], c["seed"], split, lengths, range(min(2, c["batch"])))
