@@ -647,21 +647,28 @@ def test_random_calls(i):
     xt = to_device(x)
     lt = None if c["lengths"] is None else torch.from_numpy(c["lengths"].astype(np.int32)).to(DEV)
     split, waves, kernel = c["split"], c["waves"], c["kernel"]
+    # a quarter of the calls also share thresholds between the parts of a
+    # row (drawn apart, so the draws above stay as they are)
+    share = bool(np.random.default_rng(9000 + i).random() < 0.25)
     try:
         out = ds.topk(xt, c["k"], c["B"], c["B2"], c["seed"], split=split, stats=True, waves=waves, kernel=kernel,
-                      sorted=c["sorted"], lengths=lt)
+                      sorted=c["sorted"], lengths=lt, share_threshold=share)
     except ds.DeepSelectArgumentError:
         # a forced split, wave count or kernel this shape does not allow: the
         # library's own choice must take it
         assert (split, waves, kernel) != (0, 0, 0)
         log(f"[gpu]   split={split} waves={waves} kernel={kernel} refused for this shape; library choice")
         split, waves, kernel = 0, 0, 0
-        out = ds.topk(xt, c["k"], c["B"], c["B2"], c["seed"], stats=True, sorted=c["sorted"], lengths=lt)
+        out = ds.topk(xt, c["k"], c["B"], c["B2"], c["seed"], stats=True, sorted=c["sorted"], lengths=lt,
+                      share_threshold=share)
     torch.cuda.synchronize()
     vals, idx, st = raw_of(out[0]), out[1].cpu().numpy(), out[2].cpu().numpy()
     n, k = c["n"], c["k"]
     lengths = c["lengths"] if c["lengths"] is not None else np.full(c["batch"], n)
     check_rows_len(x, vals, idx, k, lengths, sorted=c["sorted"])
+    if share:
+        log("[gpu]   shared thresholds: the cost depends on timing, the result may not")
+        return
     if split == 0:
         dcode = ds.DS_F32 if c["dt"] == "f32" else ds.DS_BF16
         split = ds.deepselect_plan_split(dcode, c["batch"], n, k, c["B"], c["B2"],
