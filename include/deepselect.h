@@ -35,6 +35,10 @@
  *     is kept per (device, stream), so calls sharing it are ordered by their
  *     stream; it is allocated (hipMalloc) the first time a shape needs it and
  *     grown when a later shape needs more.
+ *   - A call that needs no workspace (one part per row) or is given a caller
+ *     workspace enqueues kernel launches only (no allocation, no memset, no
+ *     copy), so it may be captured into a HIP graph and replayed; each replay
+ *     recomputes the result from the input as it is at replay time.
  */
 #ifndef DEEPSELECT_H
 #define DEEPSELECT_H

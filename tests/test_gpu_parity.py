@@ -674,3 +674,58 @@ def test_random_calls(i):
         split = ds.deepselect_plan_split(dcode, c["batch"], n, k, c["B"], c["B2"],
                                          torch.cuda.get_device_properties(0).multi_processor_count)
     check_stats_len(x, st, k, c["B"], c["B2"], c["seed"], split, lengths, range(min(2, c["batch"])))
+
+
+# ---------------------------------------------------------------- HIP graph capture
+
+@pytest.mark.parametrize("share", [False, True])
+def test_graph_capture_replays(share):
+    # a call with a caller workspace launches kernels only (no allocation, no
+    # memset), so it can be captured in a HIP graph; every replay, with other
+    # work and synchronisations between them, must give the eager result
+    w = synth.WORKLOADS["dsa32k"]
+    rows, S = 16, 4
+    log(f"[gpu] graph capture, split {S}, shared thresholds {share}")
+    x = synth.generate("dsa32k", rows)
+    xt = to_device(x)
+    other = to_device(synth.random_rows(rows, w.n, "f32", 5, "gauss"))
+    nbytes = ds.deepselect_workspace_bytes(ds.DS_F32, rows, w.n, w.k, w.block, w.block2, S)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    vals = torch.empty((rows, w.k), dtype=torch.float32, device=DEV)
+    idx = torch.empty((rows, w.k), dtype=torch.int32, device=DEV)
+    st = torch.empty((rows, 4), dtype=torch.int64, device=DEV)
+    o_vals = torch.empty_like(vals)
+    o_idx = torch.empty_like(idx)
+
+    def call(src, v, i, stream):
+        rc = ds.deepselect_topk_ex(src.data_ptr(), ds.DS_F32, rows, w.n, w.n, w.k, w.block, w.block2, 3,
+                                   v.data_ptr(), i.data_ptr(), stream, split=S, stats=st.data_ptr(),
+                                   workspace=ws.data_ptr(), workspace_bytes=nbytes, sorted=1,
+                                   share_threshold=int(share))
+        assert rc == 0, ds.deepselect_status_string(rc)
+
+    cur = torch.cuda.current_stream().cuda_stream
+    call(xt, vals, idx, cur)
+    torch.cuda.synchronize()
+    ref_v, ref_i, ref_st = vals.clone(), idx.clone(), st.clone()
+    check_sorted_rows(x, raw_of(ref_v), ref_i.cpu().numpy(), w.k)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(xt, vals, idx, side.cuda_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        call(xt, vals, idx, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        vals.zero_()
+        idx.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(vals, ref_v) and torch.equal(idx, ref_i), f"replay {rep} differs from the eager call"
+        if not share:  # with sharing the cost depends on timing
+            assert torch.equal(st, ref_st), f"replay {rep}: statistics differ"
+        # the program's own eager work between replays, on the same workspace
+        call(other, o_vals, o_idx, cur)
+        torch.cuda.synchronize()
