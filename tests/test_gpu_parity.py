@@ -729,3 +729,28 @@ def test_graph_capture_replays(share):
         # the program's own eager work between replays, on the same workspace
         call(other, o_vals, o_idx, cur)
         torch.cuda.synchronize()
+
+
+def test_two_streams_at_once():
+    # split calls on two streams in flight together: each stream has its own
+    # library workspace, so neither call sees the other's partial results
+    w = synth.WORKLOADS["dsa32k"]
+    rows = 12
+    log("[gpu] two streams, split rows, library workspaces")
+    xa = synth.generate("dsa32k", rows)
+    xb = synth.random_rows(rows, w.n, "f32", 9, "small_ints")
+    ta, tb = to_device(xa), to_device(xb)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    sa.wait_stream(torch.cuda.current_stream())
+    sb.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for rep in range(3):
+        with torch.cuda.stream(sa):
+            ra = ds.topk(ta, w.k, w.block, w.block2, split=4)
+        with torch.cuda.stream(sb):
+            rb = ds.topk(tb, w.k, w.block, w.block2, split=3)
+        outs.append((ra, rb))
+    torch.cuda.synchronize()
+    for ra, rb in outs:
+        check_rows(xa, raw_of(ra[0]), ra[1].cpu().numpy(), w.k)
+        check_rows(xb, raw_of(rb[0]), rb[1].cpu().numpy(), w.k)
