@@ -32,9 +32,14 @@
  *   - Every argument is checked on the host before any HIP call; a rejected call
  *     enqueues nothing. No C++ exception crosses this interface.
  *   - Entry points are thread-safe. The library-owned workspace of split rows
- *     is kept per (device, stream), so calls sharing it are ordered by their
- *     stream; it is allocated (hipMalloc) the first time a shape needs it and
- *     grown when a later shape needs more.
+ *     is kept per (device, stream) -- per thread as well for
+ *     hipStreamPerThread, whose one handle names a different stream in each
+ *     thread -- so calls sharing it are ordered by their stream; it is
+ *     allocated (hipMalloc) the first time a shape needs it and grown when a
+ *     later shape needs more. A call holds the library's workspace lock from
+ *     choosing its workspace until its kernels are queued, and a call that
+ *     grows a workspace synchronises that stream before freeing the old one,
+ *     so no queued kernel ever uses freed memory.
  *   - A call that needs no workspace (one part per row) or is given a caller
  *     workspace enqueues kernel launches only (no allocation, no memset, no
  *     copy), so it may be captured into a HIP graph and replayed; each replay
@@ -128,7 +133,9 @@ typedef struct ds_options {
      *   probs       device, batch*k floats, or NULL: the softmax of the row's
      *               results at `temperature` (exp((x_j - max)/temperature)
      *               over their sum, in float32), in output order; 0 for
-     *               fillers. A row whose largest value is -inf or NaN gets 0.
+     *               fillers. A row whose largest value is -inf or NaN gets 0;
+     *               when it is +inf, the +inf results share the mass equally
+     *               and the others get 0 (the softmax's limit).
      *   temperature > 0 (0 is read as 1).
      *   top_p       in (0, 1] (0 is read as 1): the sample is drawn from the
      *               smallest prefix of the sorted results whose probability

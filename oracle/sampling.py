@@ -11,6 +11,10 @@ The definitions the GPU's fused sampling is checked against, in float64:
   the same order: the first position whose running probability exceeds u
   times the prefix's probability.
 
+A row whose largest value is +inf takes the limit of the softmax as that
+value grows without bound: the +inf results share the mass equally and every
+other result gets 0 (the max-subtracted form would give inf - inf).
+
 The top-k step itself is the sampling use the DeepSelect deep-dive names in
 its section "算法设计背景" (top-k over vocabulary logits).
 """
@@ -32,11 +36,15 @@ def values_of(raw_row: np.ndarray) -> np.ndarray:
 
 def softmax(values_desc: np.ndarray, temperature: float = 1.0) -> np.ndarray:
     """Probabilities of values given largest first (float64). A row whose
-    largest value is not finite above -inf (or is empty) gets all zeros;
-    -inf and NaN values get probability 0."""
+    largest value is not above -inf (or is NaN, or is empty) gets all zeros;
+    -inf and NaN values get probability 0; when the largest value is +inf the
+    +inf values share the mass equally (the limit of the softmax)."""
     v = np.asarray(values_desc, dtype=np.float64)
     if len(v) == 0 or not (v[0] > -np.inf) or np.isnan(v[0]):
         return np.zeros(len(v))
+    if v[0] == np.inf:
+        e = (v == np.inf).astype(np.float64)
+        return e / e.sum()
     fin = v > -np.inf  # False for -inf and NaN
     e = np.where(fin, np.exp(np.where(fin, v - v[0], 0.0) / temperature), 0.0)
     return e / e.sum()

@@ -166,3 +166,26 @@ def test_bench_refuses_more_than_one_gpu():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_caller_outputs_are_checked():
+    # topk(out=...) hands the caller's tensors to the kernels, which write
+    # batch*k entries through them: shape, dtype, device and layout are checked
+    import torch
+
+    x = torch.zeros((3, 100), dtype=torch.bfloat16)
+    good = (torch.empty((3, 8), dtype=torch.bfloat16), torch.empty((3, 8), dtype=torch.int32))
+    assert ds._out_pair(good, x, 3, 8) == good
+    bad = [
+        (torch.empty((3, 7), dtype=torch.bfloat16), good[1]),               # too short
+        (good[0], torch.empty((2, 8), dtype=torch.int32)),                  # too few rows
+        (torch.empty((3, 8), dtype=torch.float32), good[1]),                # wrong value dtype
+        (good[0], torch.empty((3, 8), dtype=torch.int64)),                  # wrong index dtype
+        (torch.empty((8, 3), dtype=torch.bfloat16).t(), good[1]),           # strided
+        (good[0], torch.empty((3, 16), dtype=torch.int32)[:, ::2]),         # strided
+        (good[0],),                                                         # not a pair
+        None,
+    ]
+    for out in bad:
+        with pytest.raises(ValueError):
+            ds._out_pair(out, x, 3, 8)

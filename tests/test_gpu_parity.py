@@ -563,6 +563,33 @@ def test_fused_sampling_short_rows():
     check_sampling(x, vals, idx, pr.cpu().numpy(), sm.cpu().numpy(), k, u, 0.9, 0.97, lengths)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_fused_sampling_infinite_maximum(dt):
+    # rows whose largest results are +inf: those share the mass equally, the
+    # others get 0 (one +inf, three, none, and +inf next to -inf and NaN)
+    n, k, B, B2 = 2000, 32, 256, 256
+    x = synth.random_rows(4, n, dt, 23, "gauss")
+    raw = x.view(np.uint32) if dt == "f32" else x  # the bit patterns, in place
+    # +inf, -inf and a negative NaN (below -inf in key order)
+    pinf, ninf, nnan = (0x7F800000, 0xFF800000, 0xFFC00000) if dt == "f32" else (0x7F80, 0xFF80, 0xFFC0)
+    raw[0, 5] = pinf
+    raw[1, [7, 700, 1999]] = pinf
+    raw[3, [0, 1]] = pinf
+    raw[3, 2:40] = ninf
+    raw[3, 40] = nnan
+    u = np.asarray([0.1, 0.5, 0.9, 0.99], dtype=np.float32)
+    log(f"[gpu] fused sampling with +inf results ({dt})")
+    v, i, pr, sm = ds.topk_sample(to_device(x), k, B, B2, torch.from_numpy(u).to(DEV), seed=2)
+    torch.cuda.synchronize()
+    vals, idx, probs = raw_of(v), i.cpu().numpy(), pr.cpu().numpy()
+    check_sorted_rows(x, vals, idx, k)
+    check_sampling(x, vals, idx, probs, sm.cpu().numpy(), k, u, 1.0, 1.0)
+    assert probs[0, 0] == 1.0 and np.all(probs[0, 1:] == 0.0)
+    assert np.allclose(probs[1, :3], 1 / 3) and np.all(probs[1, 3:] == 0.0)
+    assert np.all(probs[3, :2] == 0.5) and np.all(probs[3, 2:] == 0.0)
+    assert np.all(np.isfinite(probs))
+
+
 # ---------------------------------------------------------------- shared thresholds
 
 SHARE = [

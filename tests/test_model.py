@@ -5,7 +5,9 @@ examples for its building blocks, the invariants and identities the
 DeepSelect deep-dive states, and the expected-work bound of its analysis.
 """
 import json
+import math
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -266,3 +268,66 @@ def test_causal_lengths_mark_the_minus_inf_tail():
     for r in range(2):
         res = model.row_topk(x[r], w.k, w.block, w.block2, seed=0, row=r, split=2, length=L[r])
         _prefix_check(x[r], L[r], w.k, res)
+
+
+# ------------------------------------------------------- the bound itself
+
+# (N, k, B, B2): the small and the long-context workloads, the logits shape
+# (ceil(N/B) = 149, floor 148), a ragged case whose ceil and floor of N/B
+# differ with k != B2 and B != B2, and one-block rows.
+_BOUND_CASES = [(4096, 64, 256, 256), (131072, 2048, 2048, 2048), (151936, 64, 1024, 1024),
+                (4097, 64, 256, 512), (1048576, 512, 1024, 1024), (100, 5, 200, 7), (200, 30, 200, 1)]
+_EULER_GAMMA = 0.57721566490153286060651209
+
+
+def _harmonic_asymptotic(m: int) -> float:
+    """H_m by the Euler-Maclaurin series ln m + gamma + 1/2m - 1/12m^2 + 1/120m^4
+    (error below 1/(252 m^6)), independent of any summation of 1/i."""
+    return math.log(m) + _EULER_GAMMA + 1 / (2 * m) - 1 / (12 * m * m) + 1 / (120 * m ** 4)
+
+
+def test_w_bound_one_block_is_the_leading_factor():
+    """m = ceil(N/B) = 1 gives H_1 = 1: the bound is exactly (1 + k/B2)(k + B + B2)."""
+    for n, k, b, b2 in [(100, 5, 200, 7), (200, 30, 200, 1), (64, 64, 64, 64)]:
+        assert model.expected_w_bound(n, k, b, b2) == pytest.approx((1 + k / b2) * (k + b + b2), rel=1e-15)
+
+
+def test_w_bound_known_harmonic_value():
+    """H_16 = 2436559/720720 (the exact rational), so the 4096-element row with
+    k = 64, B = B2 = 256 has bound 1.25 * 576 * H_16."""
+    h16 = Fraction(2436559, 720720)
+    assert sum(Fraction(1, i) for i in range(1, 17)) == h16  # the fraction itself
+    assert model.expected_w_bound(4096, 64, 256, 256) == pytest.approx(float(Fraction(5, 4) * 576 * h16),
+                                                                       rel=1e-14)
+
+
+@pytest.mark.parametrize("case", [c for c in _BOUND_CASES if -(-c[0] // c[2]) >= 16])
+def test_w_bound_matches_the_asymptotic_form(case):
+    """The boxed bound reads (1 + k/B2) L (ln m + O(1)); the O(1) is Euler's gamma
+    plus the series tail. Pins m = ceil(N/B), the factor (1 + k/B2) and L = k+B+B2."""
+    n, k, b, b2 = case
+    m = -(-n // b)
+    lead = (1 + k / b2) * (k + b + b2)
+    assert model.expected_w_bound(n, k, b, b2) / lead == pytest.approx(_harmonic_asymptotic(m), abs=1e-8)
+
+
+def test_w_bound_pins_reject_plausible_mistakes():
+    """Each plausible slip in the formula moves at least one pinned case."""
+    def exact(n, k, b, b2):
+        m = -(-n // b)
+        return float((1 + Fraction(k, b2)) * (k + b + b2) * sum(Fraction(1, i) for i in range(1, m + 1)))
+
+    def harm(m):
+        return math.fsum(1.0 / i for i in range(1, m + 1))
+
+    mutants = {
+        "m = floor(N/B)": lambda n, k, b, b2: (1 + k / b2) * (k + b + b2) * harm(max(1, n // b)),
+        "m = N": lambda n, k, b, b2: (1 + k / b2) * (k + b + b2) * harm(n),
+        "(1 + B2/k)": lambda n, k, b, b2: (1 + b2 / k) * (k + b + b2) * harm(-(-n // b)),
+        "L = k + 2B": lambda n, k, b, b2: (1 + k / b2) * (k + 2 * b) * harm(-(-n // b)),
+        "no (1 + k/B2)": lambda n, k, b, b2: (k + b + b2) * harm(-(-n // b)),
+    }
+    for name, f in mutants.items():
+        assert any(abs(f(*c) - exact(*c)) > 1e-6 * exact(*c) for c in _BOUND_CASES), name
+    for c in _BOUND_CASES:
+        assert model.expected_w_bound(*c) == pytest.approx(exact(*c), rel=1e-13), c

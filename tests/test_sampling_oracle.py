@@ -32,6 +32,17 @@ def test_softmax_closed_forms():
     assert sampling.softmax(np.array([np.nan, 1.0])).tolist() == [0.0, 0.0]
 
 
+def test_softmax_infinite_maximum_is_the_limit():
+    # the softmax of [M, M, 5, 1] as M grows tends to [1/2, 1/2, 0, 0]; the
+    # definition takes that limit when M is +inf
+    big = sampling.softmax(np.array([700.0, 700.0, 5.0, 1.0]))
+    assert np.allclose(big, [0.5, 0.5, 0.0, 0.0], atol=1e-300)
+    assert sampling.softmax(np.array([np.inf, np.inf, 5.0, 1.0, -np.inf])).tolist() == [0.5, 0.5, 0, 0, 0]
+    assert sampling.softmax(np.array([np.inf, 3.0]), 0.5).tolist() == [1.0, 0.0]
+    p = sampling.softmax(np.array([np.inf, np.inf, np.inf, 2.0]))
+    assert [sampling.sample_position(p, 1.0, u) for u in (0.0, 0.34, 0.67, 0.99)] == [0, 1, 2, 2]
+
+
 def test_nucleus_and_draw():
     p = np.array([0.5, 0.25, 0.125, 0.125])
     assert sampling.nucleus_end(p, 1.0) == 3

@@ -146,6 +146,25 @@ def _lengths_ptr(lengths, x, batch):
     return lengths.data_ptr()
 
 
+def _out_pair(out, x, batch, k):
+    """Check caller-given outputs: (vals, idx) of shape (batch, k), contiguous,
+    vals in x's dtype and idx int32, both on x's device. The kernels write
+    batch*k entries through them, so anything else is refused."""
+    import torch
+
+    try:
+        vals, idx = out
+    except (TypeError, ValueError):
+        raise ValueError("out must be a pair (vals, idx)") from None
+    for t, dt, name in ((vals, x.dtype, "vals"), (idx, torch.int32, "idx")):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"out {name} must be a tensor")
+        if tuple(t.shape) != (batch, k) or t.dtype != dt or t.device != x.device or not t.is_contiguous():
+            raise ValueError(f"out {name} must be a contiguous ({batch}, {k}) {dt} tensor on {x.device}, "
+                             f"got {tuple(t.shape)} {t.dtype} on {t.device}")
+    return vals, idx
+
+
 def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, waves: int = 0,
          kernel: int = 0, stats: bool = False, sorted: bool = False, lengths=None, share_threshold: bool = False,
          out=None, stream=None):
@@ -160,7 +179,9 @@ def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, waves: in
     (equal values by ascending column). ``lengths``: an optional int32 device
     tensor of ``batch`` valid row lengths (``ds_options_t.lengths``: row r is
     its first lengths[r] elements; outputs past a row shorter than k are index
-    -1 with value -inf). Raises on any rejected argument.
+    -1 with value -inf). ``out``: an optional (vals, idx) pair to write into,
+    contiguous (batch, k) tensors of x's dtype and int32 on x's device. Raises
+    on any rejected argument.
     """
     import torch
 
@@ -180,7 +201,7 @@ def topk(x, k: int, B: int, B2: int, seed: int = 0, *, split: int = 0, waves: in
         vals = torch.empty((batch, k), dtype=x.dtype, device=x.device)
         idx = torch.empty((batch, k), dtype=torch.int32, device=x.device)
     else:
-        vals, idx = out
+        vals, idx = _out_pair(out, x, batch, k)
     st = torch.empty((batch, DS_STATS_PER_ROW), dtype=torch.int64, device=x.device) if stats else None
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream

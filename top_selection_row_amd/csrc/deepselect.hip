@@ -43,6 +43,8 @@
 
 #include <map>
 #include <mutex>
+#include <thread>
+#include <tuple>
 #include <utility>
 
 #include "../../include/deepselect.h"
@@ -1104,8 +1106,10 @@ __device__ __forceinline__ float value_of(uint32_t raw) {
 // whose probability reaches top_p is kept, and the sample is the first
 // position whose running sum of exponentials passes u times the prefix's sum.
 // A row whose largest value is -inf or NaN (or that is empty) gets zero
-// probabilities and sample -1. Every wave takes part (workgroup barriers);
-// red is LDS scratch of NW + 4 words.
+// probabilities and sample -1; when the largest value is +inf the +inf
+// results share the mass equally and the others get 0 (the limit of the
+// softmax as the largest value grows). Every wave takes part (workgroup
+// barriers); red is LDS scratch of NW + 4 words.
 template <class D, int NW, int E>
 __device__ __forceinline__ void softmax_sample(const uint64_t (&v)[E], uint32_t i0, uint32_t cnt, const Params& p,
                                                int64_t row, uint32_t* red) {
@@ -1127,11 +1131,13 @@ __device__ __forceinline__ void softmax_sample(const uint64_t (&v)[E], uint32_t 
     lds_barrier();
     const float m = __uint_as_float(*r_max);
     const bool live = cnt > 0 && m > -__builtin_huge_valf();  // false for -inf and NaN
+    const bool pinf = m == __builtin_huge_valf();
     float ex[E], ts = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         // NaN and -inf results add nothing (-inf > -inf and NaN > -inf are false)
-        ex[e] = live && i0 + e < cnt && x[e] > -__builtin_huge_valf() ? expf((x[e] - m) * p.inv_temp) : 0.f;
+        const float w = pinf ? (x[e] == __builtin_huge_valf() ? 1.f : 0.f) : expf((x[e] - m) * p.inv_temp);
+        ex[e] = live && i0 + e < cnt && x[e] > -__builtin_huge_valf() ? w : 0.f;
         ts += ex[e];
     }
     const float incl = wave_prefix_sum_f(ts);
@@ -1881,36 +1887,45 @@ static int plan_waves(int64_t items, int32_t num_cus) { return items <= num_cus 
 struct DevInfo {
     int cus = 0;
     int lds = 0;
+    bool known = false;
 };
 
+// Devices are looked up in a fixed table (no host allocation on the call path).
+constexpr int kMaxDevices = 64;
 static std::mutex g_mu;
-static std::map<int, DevInfo> g_dev;
+static DevInfo g_dev[kMaxDevices];
+
+// Library-owned split workspaces, one per (device, stream) -- and per thread
+// for hipStreamPerThread, whose one handle names a different stream in every
+// thread. g_ws_mu is held from the choice of a workspace until the call's
+// kernels are queued, so a concurrent call that grows (frees) the same
+// workspace waits for them to be queued and then synchronises the stream.
 struct WsBuf {
     void* ptr = nullptr;
     size_t bytes = 0;
 };
-static std::map<std::pair<int, void*>, WsBuf> g_ws;
+static std::mutex g_ws_mu;
+static std::map<std::tuple<int, void*, std::thread::id>, WsBuf> g_ws;
 
 static int device_info(int dev, DevInfo& out) {
+    if (dev < 0 || dev >= kMaxDevices) return DS_ERR_HIP;
     std::lock_guard<std::mutex> lk(g_mu);
-    auto it = g_dev.find(dev);
-    if (it != g_dev.end()) {
-        out = it->second;
-        return DS_OK;
+    DevInfo& d = g_dev[dev];
+    if (!d.known) {
+        if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return DS_ERR_HIP;
+        if (hipDeviceGetAttribute(&d.lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            return DS_ERR_HIP;
+        d.known = true;
     }
-    DevInfo d;
-    if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return DS_ERR_HIP;
-    if (hipDeviceGetAttribute(&d.lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-        return DS_ERR_HIP;
-    g_dev[dev] = d;
     out = d;
     return DS_OK;
 }
 
+// Caller holds g_ws_mu (until its kernels are queued).
 static int library_workspace(int dev, hipStream_t stream, size_t bytes, void** out) {
-    std::lock_guard<std::mutex> lk(g_mu);
-    WsBuf& w = g_ws[{dev, (void*)stream}];
+    const std::thread::id tid = stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id();
+    WsBuf& w = g_ws[std::make_tuple(dev, (void*)stream, tid)];
     if (w.bytes < bytes) {
         if (w.ptr) {
             if (hipStreamSynchronize(stream) != hipSuccess) return DS_ERR_HIP;
@@ -2107,14 +2122,16 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     prm.L = L;
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    std::unique_lock<std::mutex> ws_lock;  // held while a library workspace is in use
     if (S > 1) {
         const WsLayout wl = make_ws_layout(batch, k, S);
         void* ws = nullptr;
         if (opt && opt->workspace) {
             if (opt->workspace_bytes < wl.total) return DS_ERR_WORKSPACE;
             ws = opt->workspace;
-        } else if ((st = library_workspace(dev, hs, wl.total, &ws)) != DS_OK) {
-            return st;
+        } else {
+            ws_lock = std::unique_lock<std::mutex>(g_ws_mu);
+            if ((st = library_workspace(dev, hs, wl.total, &ws)) != DS_OK) return st;
         }
         unsigned char* w = reinterpret_cast<unsigned char*>(ws);
         prm.ws_keys = reinterpret_cast<uint32_t*>(w + wl.keys);
@@ -2206,7 +2223,7 @@ const char* deepselect_status_string(int status) {
 }
 
 void deepselect_release(void) {
-    std::lock_guard<std::mutex> lk(ds::g_mu);
+    std::lock_guard<std::mutex> lk(ds::g_ws_mu);
     for (auto& kv : ds::g_ws) {
         if (kv.second.ptr) (void)hipFree(kv.second.ptr);
     }
