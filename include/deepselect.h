@@ -66,7 +66,9 @@ typedef enum {
     DS_ERR_BLOCK = -5,       /* B < 1 or B2 < 1, or a forced split the row cannot take */
     DS_ERR_UNSUPPORTED = -6, /* on-chip buffer k+B+B2 (or the block order) exceeds LDS */
     DS_ERR_HIP = -7,         /* a HIP call failed (allocation, attribute, launch) */
-    DS_ERR_WORKSPACE = -8    /* caller workspace smaller than deepselect_workspace_bytes */
+    DS_ERR_WORKSPACE = -8,   /* caller workspace smaller than deepselect_workspace_bytes */
+    DS_ERR_SCRATCH = -9      /* deepselect_topk_noalloc: the split workspace does not fit the
+                                static scratch (deepselect_scratch_bytes), or a workspace was passed */
 } ds_status_t;
 
 /* Per-row statistics written when ds_options_t.stats is set: four uint64 per row,
@@ -178,6 +180,32 @@ int deepselect_topk(const void *x, int dtype, int64_t batch, int64_t N, int64_t 
 int deepselect_topk_ex(const void *x, int dtype, int64_t batch, int64_t N, int64_t row_stride,
                        int32_t k, int32_t B, int32_t B2, uint64_t seed, void *out_vals,
                        int32_t *out_idx, void *stream, const ds_options_t *opt);
+
+/* deepselect_topk_ex for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It calls no hipMalloc, hipFree or other allocating routine. The
+ * workspace of split rows (every part's results, counts, k-th keys,
+ * statistics and shared-threshold cells) lives in a static device array of
+ * deepselect_scratch_bytes() bytes (8 MiB), one copy per GPU the library runs
+ * on, kept until the process ends; its device address is looked up once per
+ * device on the first call there. Arguments and results are those of
+ * deepselect_topk_ex with the same options, except:
+ *   - opt->workspace must be NULL (else DS_ERR_SCRATCH);
+ *   - a call whose split needs more workspace than the scratch holds
+ *     (deepselect_workspace_bytes > deepselect_scratch_bytes) returns
+ *     DS_ERR_SCRATCH with nothing enqueued; force a smaller opt->split or use
+ *     deepselect_topk_ex.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents (a call needs none from before it: the cells that must
+ * start at zero are cleared by a kernel of the call itself). Calls that may
+ * overlap on one GPU (other streams, other threads) race on it: order them.
+ * Calls with one part per row use no scratch. */
+int deepselect_topk_noalloc(const void *x, int dtype, int64_t batch, int64_t N, int64_t row_stride,
+                            int32_t k, int32_t B, int32_t B2, uint64_t seed, void *out_vals,
+                            int32_t *out_idx, void *stream, const ds_options_t *opt);
+
+/* Bytes of the static scratch deepselect_topk_noalloc uses on each GPU. */
+size_t deepselect_scratch_bytes(void);
 
 /* The split factor the library picks for this shape on a device with num_cus
  * compute units (pure host code). Returns >= 1, or a negative status. */

@@ -20,14 +20,14 @@ LIB_PATH = os.path.join(_PKG, "libdeepselect.so")
 DS_F32, DS_BF16 = 0, 1
 DS_OK = 0
 DS_ERR_NULL, DS_ERR_DTYPE, DS_ERR_SHAPE, DS_ERR_K = -1, -2, -3, -4
-DS_ERR_BLOCK, DS_ERR_UNSUPPORTED, DS_ERR_HIP, DS_ERR_WORKSPACE = -5, -6, -7, -8
+DS_ERR_BLOCK, DS_ERR_UNSUPPORTED, DS_ERR_HIP, DS_ERR_WORKSPACE, DS_ERR_SCRATCH = -5, -6, -7, -8, -9
 DS_STATS_PER_ROW = 4
 STAT_NAMES = ("W", "A", "R", "max_len")
 
 EXPORTS = (
     "deepselect_validate", "deepselect_topk", "deepselect_topk_ex", "deepselect_plan_split",
     "deepselect_workspace_bytes", "deepselect_lds_bytes", "deepselect_status_string",
-    "deepselect_release",
+    "deepselect_release", "deepselect_topk_noalloc", "deepselect_scratch_bytes",
 )
 
 
@@ -70,6 +70,11 @@ def library() -> ctypes.CDLL:
     lib.deepselect_status_string.restype = ctypes.c_char_p
     lib.deepselect_release.argtypes = []
     lib.deepselect_release.restype = None
+    lib.deepselect_topk_noalloc.argtypes = [vp, ctypes.c_int, i64, i64, i64, i32, i32, i32, u64, vp, vp, vp,
+                                            ctypes.POINTER(DsOptions)]
+    lib.deepselect_topk_noalloc.restype = ctypes.c_int
+    lib.deepselect_scratch_bytes.argtypes = []
+    lib.deepselect_scratch_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -131,6 +136,20 @@ def deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals,
                     lengths, probs, float(temperature), float(top_p), sample_u, sample_idx, int(share_threshold))
     return library().deepselect_topk_ex(x, dtype, batch, n, row_stride, k, B, B2, seed & (2**64 - 1),
                                         out_vals, out_idx, stream, ctypes.byref(opt))
+
+
+def deepselect_topk_noalloc(x, dtype, batch, n, row_stride, k, B, B2, seed, out_vals, out_idx, stream,
+                            split=0, stats=None, waves=0, kernel=0, sorted=0, lengths=None, probs=None,
+                            temperature=0.0, top_p=0.0, sample_u=None, sample_idx=None,
+                            share_threshold=0) -> int:
+    opt = DsOptions(int(split), int(waves), stats, None, 0, int(kernel), int(sorted), lengths, probs,
+                    float(temperature), float(top_p), sample_u, sample_idx, int(share_threshold))
+    return library().deepselect_topk_noalloc(x, dtype, batch, n, row_stride, k, B, B2, seed & (2**64 - 1),
+                                             out_vals, out_idx, stream, ctypes.byref(opt))
+
+
+def deepselect_scratch_bytes() -> int:
+    return library().deepselect_scratch_bytes()
 
 
 # ---------------------------------------------------------------- torch wrapper

@@ -1888,9 +1888,11 @@ struct DevInfo {
     int cus = 0;
     int lds = 0;
     bool known = false;
+    void* scratch = nullptr;  // device address of this device's copy of `scratch`
 };
 
-// Devices are looked up in a fixed table (no host allocation on the call path).
+// Devices are looked up in a fixed table (no host allocation on the call
+// path, which the allocation-free entry point relies on).
 constexpr int kMaxDevices = 64;
 static std::mutex g_mu;
 static DevInfo g_dev[kMaxDevices];
@@ -2018,11 +2020,33 @@ static int launch_all(KernelKind kind, int units, int waves, bool vec, Params pr
     return launch_kernel(deepselect_merge_kernel<DM, kGW>, prm.batch, kGW * 64, prm.L.total, st, prm);
 }
 
+// The split workspace of deepselect_topk_noalloc: a static device array,
+// one copy per GPU the library runs on, held until the process ends. Host
+// code never passes `scratch` itself to a kernel (on the host it names a
+// stand-in, not device memory): it uses the address hipGetSymbolAddress gives
+// for the current device, taken once per device.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+static int scratch_of(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return DS_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    DevInfo& d = g_dev[dev];
+    if (!d.scratch) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DS_ERR_HIP;
+        d.scratch = ptr;
+    }
+    *out = d.scratch;
+    return DS_OK;
+}
+
 static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int32_t B,
                      int32_t B2, uint64_t seed, void* out_vals, int32_t* out_idx, void* stream,
-                     const ds_options_t* opt) {
+                     const ds_options_t* opt, bool noalloc = false) {
     int st = validate_shape(dtype, batch, n, row_stride, k, B, B2);
     if (st != DS_OK) return st;
+    if (noalloc && opt && opt->workspace) return DS_ERR_SCRATCH;
     if (batch == 0) return DS_OK;
     if (!x || !out_vals || !out_idx) return DS_ERR_NULL;
     const int es = elem_bytes(dtype);
@@ -2126,7 +2150,10 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     if (S > 1) {
         const WsLayout wl = make_ws_layout(batch, k, S);
         void* ws = nullptr;
-        if (opt && opt->workspace) {
+        if (noalloc) {
+            if (wl.total > kScratchBytes) return DS_ERR_SCRATCH;
+            if ((st = scratch_of(dev, &ws)) != DS_OK) return st;
+        } else if (opt && opt->workspace) {
             if (opt->workspace_bytes < wl.total) return DS_ERR_WORKSPACE;
             ws = opt->workspace;
         } else {
@@ -2187,6 +2214,18 @@ int deepselect_topk_ex(const void* x, int dtype, int64_t batch, int64_t N, int64
     }
 }
 
+int deepselect_topk_noalloc(const void* x, int dtype, int64_t batch, int64_t N, int64_t row_stride, int32_t k,
+                            int32_t B, int32_t B2, uint64_t seed, void* out_vals, int32_t* out_idx, void* stream,
+                            const ds_options_t* opt) {
+    try {
+        return ds::topk_impl(x, dtype, batch, N, row_stride, k, B, B2, seed, out_vals, out_idx, stream, opt, true);
+    } catch (...) {
+        return DS_ERR_HIP;
+    }
+}
+
+size_t deepselect_scratch_bytes(void) { return ds::kScratchBytes; }
+
 int deepselect_plan_split(int dtype, int64_t batch, int64_t N, int32_t k, int32_t B, int32_t B2,
                           int32_t num_cus) {
     const int st = ds::validate_shape(dtype, batch, N, N, k, B, B2);
@@ -2218,6 +2257,9 @@ const char* deepselect_status_string(int status) {
         case DS_ERR_UNSUPPORTED: return "candidate buffer k+B+B2 (or the block order) does not fit in LDS";
         case DS_ERR_HIP: return "a HIP call failed";
         case DS_ERR_WORKSPACE: return "caller workspace is smaller than deepselect_workspace_bytes";
+        case DS_ERR_SCRATCH:
+            return "the call needs more split workspace than the static scratch holds (deepselect_scratch_bytes), "
+                   "or a workspace was passed to the allocation-free entry point";
         default: return "unknown status";
     }
 }
