@@ -98,6 +98,32 @@ def cpu_baseline(workload: str, seconds: float):
             "host": f"{host_cpu()}, {os.cpu_count()} logical CPUs"}
 
 
+def w_bound_row(n: int, k: int, B: int, B2: int, split: int = 1) -> float:
+    """Expected total RadixSelectTopK input of a row, (1 + k/B2)(k + B + B2) H_m
+    with m = ceil(N/B) (the DeepSelect deep-dive's boxed bound, section
+    "RadixSelectTopK 总处理元素数的期望上界"), summed over a split row's parts
+    (each with its own block count) and its merge (S blocks of k results)."""
+    def one(n_, blk):
+        m = -(-n_ // blk)
+        return (1.0 + k / B2) * (k + blk + B2) * math.fsum(1.0 / i for i in range(1, m + 1))
+
+    if split <= 1:
+        return one(n, B)
+    m = -(-n // B)
+    parts = [min((s + 1) * m // split * B, n) - s * m // split * B for s in range(split)]
+    return math.fsum(one(p, B) for p in parts) + one(split * k, k)
+
+
+def w_stats(st, n, k, B, B2, split) -> dict:
+    """Device W per row (parts and merge summed) against the bound."""
+    W = st[:, 0].astype(float)
+    bound = w_bound_row(n, k, B, B2, split)
+    return {"rows": int(len(W)), "split": int(split), "W_mean": round(float(W.mean()), 1),
+            "W_max": int(W.max()), "bound": round(bound, 1), "mean_over_bound": round(float(W.mean()) / bound, 4),
+            "max_over_bound": round(float(W.max()) / bound, 4),
+            "A_mean": round(float(st[:, 1].mean()), 1), "R_mean": round(float(st[:, 2].mean()), 2)}
+
+
 def host_cpu() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -270,6 +296,21 @@ def main() -> int:
     log(f"[bench] region {region_ms:.3f} ms for {K} steps (wall {wall * 1e3:.1f} ms): {call_ms * 1e3:.2f} us per "
         f"call, {achieved:.0f} GB/s; per-call event pairs: median {pair_ms[P // 2] * 1e3:.2f} us")
 
+    # one more call, untimed, with the device statistics: W against the bound
+    st_dev = torch.empty((w.batch, 4), dtype=torch.int64, device=dev)
+    opt_st = ds.DsOptions(int(split), int(args.waves), st_dev.data_ptr(), None, 0, int(args.kernel),
+                          int(args.sorted), lens.data_ptr() if lens is not None else None, None, 1.0, 1.0, None,
+                          None, 0)
+    rc = fn(ptrs[0], dt, w.batch, w.n, w.n, w.k, w.block, w.block2, seed, vptr, iptr, sptr, ctypes.byref(opt_st))
+    if rc != 0:
+        raise RuntimeError(f"deepselect_topk_ex failed: {ds.deepselect_status_string(rc)}")
+    torch.cuda.synchronize()
+    wst = w_stats(st_dev.cpu().numpy(), w.n, w.k, w.block, w.block2, split)
+    if args.lengths:
+        wst["note"] = "rows run on their valid prefixes; the bound is for full rows"
+    log(f"[bench] W per row: mean {wst['W_mean']}, max {wst['W_max']}, bound {wst['bound']} "
+        f"(mean/bound {wst['mean_over_bound']})")
+
     torch_info = None
     if not args.no_torch:
         tk = {}
@@ -320,6 +361,7 @@ def main() -> int:
                       "event_pair_median": round(pair_ms[P // 2] * 1e3, 3), "event_pairs": P},
         "cpu_baseline": cpu,
         "torch_topk": torch_info,
+        "w_stats": wst,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -273,6 +273,22 @@ def expected_w_bound(n: int, k: int, block: int, block2: int) -> float:
     return (1.0 + k / block2) * (k + block + block2) * harmonic
 
 
+def expected_w_bound_row(n: int, k: int, block: int, block2: int, split: int = 1) -> float:
+    """The bound summed over a row cut into ``split`` parts (reading c12):
+    every part is a DeepSelect on its own blocks [s*m//S, (s+1)*m//S), so it
+    has the boxed bound with its own m_s (its element count over B, rounded
+    up), and the merge is a DeepSelect over S blocks of k results (block
+    length k, the same k and B2)."""
+    if split <= 1:
+        return expected_w_bound(n, k, block, block2)
+    m = -(-n // block)
+    total = 0.0
+    for b0, b1 in part_bounds(m, split):
+        n_s = min(b1 * block, n) - b0 * block
+        total += expected_w_bound(n_s, k, block, block2)
+    return total + expected_w_bound(split * k, k, k, block2)
+
+
 def batch_topk(x: np.ndarray, k: int, block: int, block2: int, seed: int = 0, split: int = 1,
                row0: int = 0, lengths=None):
     """Model over every row of ``x``; ``row0`` is the row number of x[0] (block order)."""
@@ -282,5 +298,5 @@ def batch_topk(x: np.ndarray, k: int, block: int, block2: int, seed: int = 0, sp
 
 
 __all__ = ["inclusive_scan", "exclusive_scan", "compact", "splitmix64", "block_order",
-           "radix_select_topk", "deepselect", "row_topk", "batch_topk", "expected_w_bound",
+           "radix_select_topk", "deepselect", "row_topk", "batch_topk", "expected_w_bound", "expected_w_bound_row",
            "part_bounds", "RunStats", "RowResult", "F32", "BF16"]

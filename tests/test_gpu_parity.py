@@ -133,6 +133,28 @@ def test_workload_full_size(name):
     assert np.all(st[:, 3] <= max(w.k + w.block + w.block2 - 1, 2 * w.k + w.block2 - 1))
 
 
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_device_w_within_the_bound(name):
+    # the boxed bound (the deep-dive's section "RadixSelectTopK 总处理元素数的期望上界")
+    # is an expectation over the random block order: the device's W per row,
+    # averaged over rows and seeds 0, 1, 2, stays at or below it (for split
+    # rows the parts' bounds plus the merge's, at the library's split)
+    w = synth.WORKLOADS[name]
+    x = synth.generate(name)
+    xt = to_device(x)
+    S = plan(w)
+    ws = []
+    for seed in (0, 1, 2):
+        out = ds.topk(xt, w.k, w.block, w.block2, seed, stats=True)
+        torch.cuda.synchronize()
+        ws.append(out[2].cpu().numpy()[:, 0].astype(np.float64))
+    W = np.concatenate(ws)
+    bound = model.expected_w_bound_row(w.n, w.k, w.block, w.block2, S)
+    log(f"[gpu] W {name} split {S}: mean {W.mean():.0f} max {W.max():.0f} bound {bound:.0f} "
+        f"(mean/bound {W.mean() / bound:.3f}, max/bound {W.max() / bound:.3f})")
+    assert W.mean() <= bound
+
+
 @pytest.mark.parametrize("name,split", [("dsa32k", 1), ("dsa32k", 2), ("dsa32k", 8),
                                         ("dsa128k_bf16", 1), ("dsa128k_bf16", 4),
                                         ("asc1m_b1", 8), ("asc1m_b1", 64), ("gauss4k", 3),

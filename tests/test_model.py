@@ -331,3 +331,30 @@ def test_w_bound_pins_reject_plausible_mistakes():
         assert any(abs(f(*c) - exact(*c)) > 1e-6 * exact(*c) for c in _BOUND_CASES), name
     for c in _BOUND_CASES:
         assert model.expected_w_bound(*c) == pytest.approx(exact(*c), rel=1e-13), c
+
+
+def test_w_bound_of_split_rows():
+    """Split rows (reading c12): the parts' bounds with their own m_s plus the
+    merge's, a DeepSelect over S blocks of k. Worked by hand for a 4096-element
+    row, k = 64, B = B2 = 256, S = 2: two parts of 8 blocks (H_8 = 761/280)
+    and a merge of two blocks of 64 (H_2 = 3/2, L = 64 + 64 + 256)."""
+    want = 2 * Fraction(5, 4) * 576 * Fraction(761, 280) + Fraction(5, 4) * 384 * Fraction(3, 2)
+    assert model.expected_w_bound_row(4096, 64, 256, 256, 2) == pytest.approx(float(want), rel=1e-13)
+    assert model.expected_w_bound_row(4096, 64, 256, 256, 1) == model.expected_w_bound(4096, 64, 256, 256)
+    # uneven parts: 17 blocks (the last holds 1 element) over 3 parts of 5, 6 and 6 blocks
+    n, k, b, b2 = 4097, 16, 256, 128
+    parts = [(0, 5), (5, 11), (11, 17)]
+    assert model.part_bounds(17, 3) == parts
+    hm = lambda m: sum(Fraction(1, i) for i in range(1, m + 1))
+    lead = (1 + Fraction(k, b2)) * (k + b + b2)
+    want = lead * (hm(5) + hm(6) + hm(6)) + (1 + Fraction(k, b2)) * (k + k + b2) * hm(3)
+    assert model.expected_w_bound_row(n, k, b, b2, 3) == pytest.approx(float(want), rel=1e-13)
+
+
+def test_split_rows_mean_w_below_their_bound():
+    """The model's W of split rows (parts plus merge) stays under the summed bound."""
+    for name, split in [("dsa32k", 4), ("dsa128k_bf16", 2), ("asc1m", 8)]:
+        w = synth.WORKLOADS[name]
+        x = synth.generate(name, 1)
+        ws = [model.row_topk(x[0], w.k, w.block, w.block2, seed=s, split=split).stats.W for s in range(3)]
+        assert np.mean(ws) <= model.expected_w_bound_row(w.n, w.k, w.block, w.block2, split), name

@@ -70,3 +70,14 @@ def test_trace_per_call_total(tmp_path, capsys):
 def test_source_digest_is_stable():
     assert profiling.source_digest() == profiling.source_digest()
     assert len(profiling.source_digest()) == 16
+
+
+def test_bench_w_bound_matches_the_model():
+    # bench.py states the bound for its report; the oracle's model is the pinned one
+    import bench
+    from oracle import model
+
+    for n, k, b, b2, split in [(4096, 64, 256, 256, 1), (131072, 2048, 2048, 2048, 2), (32768, 512, 1024, 1024, 4),
+                               (1048576, 512, 1024, 1024, 16), (151936, 64, 1024, 1024, 1), (4097, 16, 256, 128, 3)]:
+        assert bench.w_bound_row(n, k, b, b2, split) == pytest.approx(
+            model.expected_w_bound_row(n, k, b, b2, split), rel=1e-12)

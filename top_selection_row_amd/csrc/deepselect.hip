@@ -79,7 +79,33 @@ struct Params {
     Layout L;
 };
 
+// Optional cycle accounting (builds with -DDS_PROFILE only): each wave adds
+// the shader-clock cycles between probes to the category of the phase that
+// just ended and leaves them in ds_prof[workgroup][wave][category].
+#ifdef DS_PROFILE
+constexpr int kProfCats = 16, kProfWaves = 8, kProfGroups = 4096;
+__device__ unsigned long long ds_prof[kProfGroups * kProfWaves * kProfCats];
+#define DS_PROF(st, cat) (st).prof_mark(cat)
+#else
+#define DS_PROF(st, cat) ((void)0)
+#endif
+
 struct RunState {
+#ifdef DS_PROFILE
+    uint64_t pt_last = __builtin_amdgcn_s_memtime();
+    uint64_t pt[kProfCats] = {};
+    __device__ void prof_mark(int cat) {
+        const uint64_t now = __builtin_amdgcn_s_memtime();
+        pt[cat] += now - pt_last;
+        pt_last = now;
+    }
+    __device__ void prof_flush() {
+        if ((threadIdx.x & 63) == 0 && blockIdx.x < (unsigned)kProfGroups) {
+            unsigned long long* o = ds_prof + ((size_t)blockIdx.x * kProfWaves + (threadIdx.x >> 6)) * kProfCats;
+            for (int i = 0; i < kProfCats; ++i) atomicAdd(&o[i], (unsigned long long)pt[i]);
+        }
+    }
+#endif
     uint32_t len = 0;   // candidate entries
     bool tset = false;  // threshold set (a compaction happened)
     uint32_t tkey = 0;  // threshold key
@@ -167,9 +193,11 @@ __device__ __forceinline__ void select_buffer(Lds<D>& s, RunState& st, uint32_t 
 // Compaction inside the loop (counts in W and R).
 template <class D, int NW>
 __device__ __forceinline__ void compact(Lds<D>& s, RunState& st, uint32_t k) {
+    DS_PROF(st, 14);
     st.W += st.len;
     st.R += 1;
     select_buffer<D, NW>(s, st, k);
+    DS_PROF(st, 13);
 }
 
 // Final RadixSelectTopK (its input length counts in W); ends with a barrier.
@@ -790,7 +818,9 @@ struct RingStreamer {
         const uint32_t incl = wave_prefix_sum(lc);
         const uint32_t c = uniform(__builtin_amdgcn_readlane(incl, 63));
         if (lane_id() == 0) s.cnt[st.par * NW + w] = c;
+        DS_PROF(st, 2);
         lds_barrier();
+        DS_PROF(st, 3);
         // the pages' order: block after block, compaction check after each.
         // Lane g < NW takes block g's count (0 outside [first, nblk)); a
         // prefix sum over those lanes gives the length after each block, the
@@ -831,6 +861,7 @@ struct RingStreamer {
         st.A += run - st.len;
         st.maxlen = run > st.maxlen ? run : st.maxlen;
         st.len = run;
+        DS_PROF(st, 4);
         return trig;
     }
 
@@ -862,8 +893,10 @@ struct RingStreamer {
             const int32_t nblk = ms - stp * NW < NW ? ms - stp * NW : NW;  // blocks in this step
             uint32_t boff, blen;
             block_at(stp * NW + w, boff, blen);
+            DS_PROF(st, 14);
             wait_block(issued - 1 - stp);
             read_slot(q, r);
+            DS_PROF(st, 1);
             if (share && shared != 0u) {
                 // another part's threshold (any part's k-th is at most the
                 // row's) raises the filter of this wave's next blocks
@@ -1295,10 +1328,15 @@ __device__ __forceinline__ void write_part(Lds<D>& s, const RunState& st, const 
         p.ws_tkey[slot] = st.len == (uint32_t)p.k && st.tset ? st.tkey : 0u;
     }
     if constexpr (is_packed<D>::value) {
-        for (int64_t j = threadIdx.x; j < p.k; j += NW * 64) {
-            const uint32_t e = s.keys[j];
-            p.ws_keys[slot * p.k + j] = e >> 16;
-            p.ws_idx[slot * p.k + j] = part_elem0 + (e & 0xFFFFu);
+        // packed bfloat16 results stay one word each, key << 16 | column
+        // inside the part (the merge adds the part's first column): 4 bytes
+        // a result, 16-byte stores when k allows
+        (void)part_elem0;
+        if (p.k % 4 == 0) {
+            for (int64_t j = (int64_t)threadIdx.x * 4; j < p.k; j += NW * 64 * 4)
+                *reinterpret_cast<u32x4*>(p.ws_keys + slot * p.k + j) = *reinterpret_cast<const u32x4*>(&s.keys[j]);
+        } else {
+            for (int64_t j = threadIdx.x; j < p.k; j += NW * 64) p.ws_keys[slot * p.k + j] = s.keys[j];
         }
     } else if (p.k % 4 == 0) {  // the workspace arrays are 256-byte aligned
         for (int64_t j = (int64_t)threadIdx.x * 4; j < p.k; j += NW * 64 * 4) {
@@ -1409,9 +1447,10 @@ __global__ __launch_bounds__(NW * 64) void deepselect_ring_kernel(Params p) {
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const PartGeom g = part_geom(p, item);
         lds_barrier();  // LDS free from the previous item
+        RunState st;
         begin_item<D, NW>(s);
         build_order<NW>(s.perm, p.seed, g.row, 0, g.b0, g.ms, s.base);
-        RunState st;
+        DS_PROF(st, 0);
         RingStreamer<D, NW, U> sm{s,
                                   st,
                                   part_rsrc<D>(p, g),
@@ -1426,11 +1465,17 @@ __global__ __launch_bounds__(NW * 64) void deepselect_ring_kernel(Params p) {
                                   ring,
                                   p.ws_share ? p.ws_share + g.row : nullptr};
         sm.run();
+        DS_PROF(st, 14);
         final_select<D, NW>(s, st, (uint32_t)p.k);
+        DS_PROF(st, 11);
         if (p.split == 1)
             write_row<D, NW>(s, p, g.row, st.len, st.W, st.A, st.R, st.maxlen);
         else
             write_part<D, NW>(s, st, p, g.slot, (uint32_t)g.part_elem0);
+        DS_PROF(st, 12);
+#ifdef DS_PROFILE
+        st.prof_flush();
+#endif
     }
 }
 
@@ -1657,33 +1702,46 @@ struct MergeTile {
     uint32_t key[kMT], col[kMT];
 };
 
-// Tile t of part `part`'s results (lanes contiguous per load).
-template <int NW>
+// Tile t of part `part`'s results (lanes contiguous per load). kPkParts:
+// the parts wrote packed bfloat16 words, key << 16 | column inside the part,
+// whose first column is added back here.
+template <int NW, bool kPkParts>
 __device__ __forceinline__ void load_part_tile(MergeTile& t, const Params& p, int64_t row, int64_t part,
                                                uint32_t tile) {
     constexpr uint32_t TE = NW * 64 * kMT;
     const uint32_t k = (uint32_t)p.k;
     const uint32_t t0 = tile * TE;
     const int64_t off = (row * p.split + part) * (int64_t)k + t0;
+    uint32_t col0 = 0;
+    if constexpr (kPkParts) {
+        const int64_t m = p.lengths ? ceil_div(row_len(p, row), (int64_t)p.B) : p.m;
+        col0 = (uint32_t)(part_begin(m, part, p.split) * p.B);
+    }
 #pragma unroll
     for (int q = 0; q < kMT; ++q) {
         const uint32_t e = (uint32_t)q * NW * 64 + (uint32_t)threadIdx.x;
         const bool inb = t0 + e < k;
-        t.key[q] = inb ? p.ws_keys[off + e] : 0u;
-        t.col[q] = inb ? p.ws_idx[off + e] : 0u;
+        if constexpr (kPkParts) {
+            const uint32_t w = inb ? p.ws_keys[off + e] : 0u;
+            t.key[q] = w >> 16;
+            t.col[q] = col0 + (w & 0xFFFFu);
+        } else {
+            t.key[q] = inb ? p.ws_keys[off + e] : 0u;
+            t.col[q] = inb ? p.ws_idx[off + e] : 0u;
+        }
     }
 }
 
 // Tile number `tile` of the merge: tile tile % tpp of the part at order
 // position tile / tpp.
-template <int NW>
+template <int NW, bool kPkParts>
 __device__ __forceinline__ void load_merge_tile(MergeTile& t, const Params& p, const uint16_t* perm, int64_t row,
                                                 int64_t tile, uint32_t tpp) {
     const int64_t i = tile / tpp;
-    load_part_tile<NW>(t, p, row, (int64_t)uniform(perm[i]), (uint32_t)(tile - i * tpp));
+    load_part_tile<NW, kPkParts>(t, p, row, (int64_t)uniform(perm[i]), (uint32_t)(tile - i * tpp));
 }
 
-template <class D, int NW>
+template <class D, int NW, bool kPkParts>
 __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     Lds<D> s = lds_of<D>(smem, p.L);
@@ -1698,8 +1756,8 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
     for (int64_t row = blockIdx.x; row < p.batch; row += gridDim.x) {
         MergeTile cur, nxt, pre0, pre1;
         if (both) {
-            load_part_tile<NW>(pre0, p, row, 0, 0);
-            load_part_tile<NW>(pre1, p, row, 1, 0);
+            load_part_tile<NW, kPkParts>(pre0, p, row, 0, 0);
+            load_part_tile<NW, kPkParts>(pre1, p, row, 1, 0);
         }
         // the parts' result counts (short or filtered parts), lane q holding
         // part q's, loaded with the first tiles (more than 64 parts: read
@@ -1725,10 +1783,10 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
             nxt = swap ? pre0 : pre1;
         } else {
             build_order<NW>(s.perm, p.seed, row, 1, 0, S, s.base);
-            load_merge_tile<NW>(cur, p, s.perm, row, 0, tpp);
+            load_merge_tile<NW, kPkParts>(cur, p, s.perm, row, 0, tpp);
         }
         for (int64_t j = 0; j < tiles; ++j) {
-            if (!both && j + 1 < tiles) load_merge_tile<NW>(nxt, p, s.perm, row, j + 1, tpp);
+            if (!both && j + 1 < tiles) load_merge_tile<NW, kPkParts>(nxt, p, s.perm, row, j + 1, tpp);
             const uint32_t t0 = (uint32_t)(j % tpp) * TE;
             // results of the part: k, or fewer for a part shorter than k or
             // one filtered by a shared threshold
@@ -2013,11 +2071,13 @@ static int launch_all(KernelKind kind, int units, int waves, bool vec, Params pr
     if (prm.sorted) M8 = with_sort(M8, prm.k);
     if (prm.k > kGW * 64 * kMT && M8.total <= kLdsLimit) {
         prm.L = M8;
-        return launch_kernel(deepselect_merge_kernel<DM, 8>, prm.batch, 8 * 64, prm.L.total, st, prm);
+        return launch_kernel(deepselect_merge_kernel<DM, 8, is_packed<D>::value>, prm.batch, 8 * 64, prm.L.total,
+                             st, prm);
     }
     prm.L = make_merge_layout(dtype, prm.k, prm.B2, prm.split, kGW);
     if (prm.sorted) prm.L = with_sort(prm.L, prm.k);
-    return launch_kernel(deepselect_merge_kernel<DM, kGW>, prm.batch, kGW * 64, prm.L.total, st, prm);
+    return launch_kernel(deepselect_merge_kernel<DM, kGW, is_packed<D>::value>, prm.batch, kGW * 64, prm.L.total, st,
+                         prm);
 }
 
 // The split workspace of deepselect_topk_noalloc: a static device array,
@@ -2225,6 +2285,19 @@ int deepselect_topk_noalloc(const void* x, int dtype, int64_t batch, int64_t N, 
 }
 
 size_t deepselect_scratch_bytes(void) { return ds::kScratchBytes; }
+
+#ifdef DS_PROFILE
+// Profiling builds only: copy out (and clear) the per-wave cycle counts.
+int ds_prof_read(void* host, size_t bytes, int clear) {
+    if (hipDeviceSynchronize() != hipSuccess) return DS_ERR_HIP;
+    if (hipMemcpyFromSymbol(host, HIP_SYMBOL(ds::ds_prof), bytes) != hipSuccess) return DS_ERR_HIP;
+    void* p = nullptr;
+    if (clear && (hipGetSymbolAddress(&p, HIP_SYMBOL(ds::ds_prof)) != hipSuccess ||
+                  hipMemset(p, 0, sizeof(ds::ds_prof)) != hipSuccess))
+        return DS_ERR_HIP;
+    return hipDeviceSynchronize() == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+#endif
 
 int deepselect_plan_split(int dtype, int64_t batch, int64_t N, int32_t k, int32_t B, int32_t B2,
                           int32_t num_cus) {
