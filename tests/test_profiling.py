@@ -81,3 +81,15 @@ def test_bench_w_bound_matches_the_model():
                                (1048576, 512, 1024, 1024, 16), (151936, 64, 1024, 1024, 1), (4097, 16, 256, 128, 3)]:
         assert bench.w_bound_row(n, k, b, b2, split) == pytest.approx(
             model.expected_w_bound_row(n, k, b, b2, split), rel=1e-12)
+
+
+def test_sq_ratios():
+    cs = {"SQ_WAVES": 4.0, "SQ_WAVE_CYCLES": 1000.0, "SQ_INSTS_VALU": 400.0, "SQ_ACTIVE_INST_VALU": 200.0,
+          "SQ_THREAD_CYCLES_VALU": 6400.0, "SQ_ACTIVE_INST_LDS": 50.0, "SQ_LDS_BANK_CONFLICT": 25.0,
+          "SQ_WAIT_ANY": 600.0}
+    d = profiling.sq_derived(cs)
+    assert d["insts_valu_per_wave"] == 100.0
+    assert d["valu_active_share"] == 0.2
+    assert d["valu_lane_utilisation"] == 0.5
+    assert d["lds_bank_conflict_per_active_cycle"] == 0.5
+    assert d["wait_any_share"] == 0.6

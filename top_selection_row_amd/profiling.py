@@ -21,6 +21,19 @@ Commands (each summary records the full command lines that produced it):
       FETCH_SIZE and WRITE_SIZE, each scaled by what the same counter reads for
       a plain copy kernel of known size (bytes read = bytes written = N per
       copy).
+
+  python -m top_selection_row_amd.profiling collect --workload W --raw DIR \
+        --out profiles [--tag T] [-- extra bench.py arguments]
+      runs every pass on a GPU host, each a child process: the kernel trace,
+      FETCH_SIZE and WRITE_SIZE of bench.py and of its 512 MiB copy, and two
+      passes of SQ counters (instruction mix, VALU and LDS activity, waits, LDS
+      bank and address conflicts); writes deepselect_<tag>_trace.txt,
+      deepselect_<tag>_traffic.json and deepselect_<tag>_sq.txt to --out.
+
+  python -m top_selection_row_amd.profiling table --out FILE [--workloads ...]
+      runs bench.py once per workload (library choices, torch.topk beside it)
+      and writes the table of per-call time, throughput, fraction of the HBM
+      peak and W against its bound.
 """
 from __future__ import annotations
 
@@ -170,6 +183,142 @@ def cmd_traffic(a):
     print(text)
 
 
+SQ_PASSES = [
+    ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS",
+     "SQ_ACTIVE_INST_VALU", "SQ_THREAD_CYCLES_VALU"],
+    ["SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT",
+     "SQ_LDS_ADDR_CONFLICT", "SQ_INSTS_LDS_ATOMIC", "SQ_ACTIVE_INST_SCA"],
+]
+
+
+def sq_derived(cs: dict) -> dict:
+    """Ratios of one kernel's SQ counters (each a sum over waves and instances)."""
+    out = {}
+    waves = cs.get("SQ_WAVES", 0.0)
+    wc = cs.get("SQ_WAVE_CYCLES", 0.0)
+    if waves:
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_LDS_ATOMIC"):
+            if c in cs:
+                out[f"{c[3:].lower()}_per_wave"] = cs[c] / waves
+    if wc:
+        for c, name in (("SQ_ACTIVE_INST_VALU", "valu_active_share"), ("SQ_ACTIVE_INST_LDS", "lds_active_share"),
+                        ("SQ_ACTIVE_INST_SCA", "salu_active_share"), ("SQ_WAIT_ANY", "wait_any_share"),
+                        ("SQ_WAIT_INST_ANY", "wait_inst_any_share"), ("SQ_WAIT_INST_LDS", "wait_inst_lds_share")):
+            if c in cs:
+                out[name] = cs[c] / wc
+    if cs.get("SQ_ACTIVE_INST_VALU"):
+        # active lanes per VALU instruction cycle, over 64
+        out["valu_lane_utilisation"] = cs.get("SQ_THREAD_CYCLES_VALU", 0.0) / (64.0 * cs["SQ_ACTIVE_INST_VALU"])
+    if cs.get("SQ_ACTIVE_INST_LDS"):
+        out["lds_bank_conflict_per_active_cycle"] = cs.get("SQ_LDS_BANK_CONFLICT", 0.0) / cs["SQ_ACTIVE_INST_LDS"]
+        out["lds_addr_conflict_per_active_cycle"] = cs.get("SQ_LDS_ADDR_CONFLICT", 0.0) / cs["SQ_ACTIVE_INST_LDS"]
+    return out
+
+
+def _run(cmd, log, timeout):
+    import subprocess
+
+    log.append(" ".join(cmd))
+    print("[collect] " + " ".join(cmd), flush=True)
+    res = subprocess.run(cmd, cwd="/tmp", env=dict(os.environ, TMPDIR="/tmp"), timeout=timeout,
+                         stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        print(res.stdout[-3000:], flush=True)
+        raise RuntimeError(f"step failed ({res.returncode}): {' '.join(cmd)}")
+    return res.stdout
+
+
+def cmd_collect(a):
+    bench = os.path.join(ROOT, "bench.py")
+    raw = os.path.abspath(a.raw)
+    out = os.path.abspath(a.out)
+    os.makedirs(raw, exist_ok=True)
+    os.makedirs(out, exist_ok=True)
+    tag = a.tag or a.workload
+    extra = list(a.extra or [])
+    py = sys.executable
+    bargs = [py, bench, "--workload", a.workload, "--no-cpu-baseline", "--no-torch"] + extra
+    prof = ["rocprofv3"]
+    cmds = []
+    # 1. kernel trace
+    _run(prof + ["--kernel-trace", "--stats", "--output-format", "csv", "-d", f"{raw}/trace", "-o", "trace", "--"]
+         + bargs + ["--steps", str(a.steps), "--warmup", "20"], cmds, 300)
+    tr = argparse.Namespace(dir=f"{raw}/trace", title=f"DeepSelect {tag}: rocprofv3 kernel trace",
+                            cmd=f"python -m top_selection_row_amd.profiling collect {' '.join(sys.argv[2:])} "
+                                f"(pass: {cmds[-1]})", match="deepselect")
+    import contextlib
+    import io
+
+    buf = io.StringIO()
+    with contextlib.redirect_stdout(buf):
+        cmd_trace(tr)
+    with open(os.path.join(out, f"deepselect_{tag}_trace.txt"), "w") as f:
+        f.write(buf.getvalue())
+    # 2. traffic: FETCH_SIZE and WRITE_SIZE of the call and of a known copy
+    dirs = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        for what, args in (("kernel", bargs + ["--steps", "50", "--warmup", "5"]),
+                           ("copy", [py, bench, "--mode", "copy", "--copy-mb", "512", "--steps", "20", "--warmup", "3"])):
+            d = f"{raw}/pmc_{ctr}_{what}"
+            _run(prof + ["--pmc", ctr, "--output-format", "csv", "-d", d, "-o", "pmc", "--"] + args, cmds, 180)
+            dirs[(ctr, what)] = d
+    tf = argparse.Namespace(workload=a.workload, kernel_fetch=dirs[("FETCH_SIZE", "kernel")],
+                            kernel_write=dirs[("WRITE_SIZE", "kernel")], copy_fetch=dirs[("FETCH_SIZE", "copy")],
+                            copy_write=dirs[("WRITE_SIZE", "copy")], copy_bytes=512.0 * 2**20,
+                            cmd=[f"python -m top_selection_row_amd.profiling collect {' '.join(sys.argv[2:])}"]
+                            + cmds[-4:], out=os.path.join(out, f"deepselect_{tag}_traffic.json"))
+    with contextlib.redirect_stdout(io.StringIO()):
+        cmd_traffic(tf)
+    # 3. SQ counters, two passes
+    merged = defaultdict(dict)
+    for i, ctrs in enumerate(SQ_PASSES):
+        d = f"{raw}/sq{i}"
+        _run(prof + ["--pmc"] + ctrs + ["--output-format", "csv", "-d", d, "-o", "pmc", "--"]
+             + bargs + ["--steps", "20", "--warmup", "5"], cmds, 180)
+        for k, cs in counters(d, "deepselect").items():
+            merged[k].update(cs)
+    lines = [f"# DeepSelect {tag}: SQ counters per dispatch (summed over the kernel's waves and instances)",
+             f"# command: python -m top_selection_row_amd.profiling collect {' '.join(sys.argv[2:])}"]
+    lines += [f"#   pass: {c}" for c in cmds[-2:]]
+    for k, cs in merged.items():
+        lines.append(f"== {k}")
+        for c, v in sorted(cs.items()):
+            lines.append(f"   {c:34s} {v:16.1f}")
+        for c, v in sq_derived(cs).items():
+            lines.append(f"   {c:34s} {v:16.4f}")
+    with open(os.path.join(out, f"deepselect_{tag}_sq.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+
+
+def cmd_table(a):
+    bench = os.path.join(ROOT, "bench.py")
+    rows = []
+    for wl in a.workloads:
+        cmd = [sys.executable, bench, "--workload", wl, "--no-cpu-baseline", "--steps", str(a.steps),
+               "--warmup", "20"]
+        txt = _run(cmd, [], 300)
+        line = [l for l in txt.splitlines() if l.startswith("{")][-1]
+        rows.append(json.loads(line))
+    out = ["# DeepSelect on one MI355X, every workload (library choice of split and waves)",
+           f"# command: python -m top_selection_row_amd.profiling table {' '.join(sys.argv[2:])}",
+           "# (each row: python3 bench.py --workload W --no-cpu-baseline; per-call time = K calls back to back",
+           "# between two HIP events on the launch stream; torch.topk on the same rotating buffers)", "",
+           "| workload | batch x N, dtype | k | split | us per call | Gelem/s | GB/s | frac of 8 TB/s "
+           "| torch.topk us (unsorted / sorted) | W mean / bound (max / bound) |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    for d in rows:
+        c, w, t = d["config"], d["w_stats"], d.get("torch_topk") or {}
+        out.append(f"| {c['workload']} | {c['batch']} x {c['N']} {c['input_dtype']} | {c['k']} | {c['split']} "
+                   f"| {d['kernel_us']['avg']:.2f} | {d['value']:.1f} | {d['roofline']['achieved']:.0f} "
+                   f"| {d['roofline']['frac']:.4f} | {t.get('unsorted_us', '-')} / {t.get('sorted_us', '-')} "
+                   f"| {w['mean_over_bound']:.3f} ({w['max_over_bound']:.3f}) |")
+    text = "\n".join(out) + "\n"
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(text, flush=True)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="what", required=True)
@@ -194,6 +343,20 @@ def main(argv=None):
     r.add_argument("--cmd", default="", nargs="*")
     r.add_argument("--out", default="")
     r.set_defaults(fn=cmd_traffic)
+    co = sub.add_parser("collect")
+    co.add_argument("--workload", required=True)
+    co.add_argument("--raw", required=True, help="directory for rocprofv3's raw output")
+    co.add_argument("--out", required=True, help="directory for the summaries")
+    co.add_argument("--tag", default="")
+    co.add_argument("--steps", type=int, default=200)
+    co.add_argument("extra", nargs="*", help="more bench.py arguments (after --)")
+    co.set_defaults(fn=cmd_collect)
+    tb = sub.add_parser("table")
+    tb.add_argument("--out", required=True)
+    tb.add_argument("--steps", type=int, default=200)
+    tb.add_argument("--workloads", nargs="*", default=["gauss4k", "dsa32k", "dsa128k_bf16", "vocab152k_k64",
+                                                       "vocab152k_k1024", "asc1m", "ties1m", "asc1m_b1"])
+    tb.set_defaults(fn=cmd_table)
     a = ap.parse_args(argv)
     a.fn(a)
     return 0
