@@ -35,7 +35,9 @@ Readings of points the pages leave open (each one is also listed in the design doc):
   each part's top-k gathered and reduced to the row's top-k): part s of S owns
   the contiguous blocks [s*m//S, (s+1)*m//S) and runs DeepSelect on them; the
   merge runs DeepSelect again with one block per part (its k results), in the
-  random order of tag 1, and the same k and B2.
+  random order of tag 1, and the same k and B2, with T starting just below the
+  largest k-th key among the parts that hold k results (a part's k-th never
+  exceeds the row's, so nothing below it can be among the row's top k).
 """
 from __future__ import annotations
 
@@ -165,6 +167,7 @@ class RunStats:
     max_len: int = 0
     thresholds: list = field(default_factory=list)
     all_admitted_before_first_compaction: bool = True
+    selected: bool = False  # some RadixSelectTopK call had more than k entries (T was set)
 
     def add(self, o: "RunStats"):
         self.W += o.W
@@ -175,18 +178,20 @@ class RunStats:
         self.all_admitted_before_first_compaction &= o.all_admitted_before_first_compaction
 
 
-def deepselect(blocks, k: int, block2: int, bits: int):
+def deepselect(blocks, k: int, block2: int, bits: int, t0=None):
     """DeepSelectTopk over ``blocks`` (a list of (keys, idx) already in scan order).
 
     Returns (keys, idx, kth, stats). The loop follows the pseudo-code: filter
     each block against T (everything admitted while T is unset), append the
     survivors, and compact with RadixSelectTopK whenever len >= k + B2; at the
-    end RadixSelectTopK once more.
+    end RadixSelectTopK once more. ``t0``: a key every wanted result is known
+    to reach; T then starts just below it (keys >= t0 are admitted from the
+    first block) instead of unset.
     """
     st = RunStats()
     ck = np.empty(0, dtype=np.uint32)
     ci = np.empty(0, dtype=np.int64)
-    T = None
+    T = None if not t0 else int(t0) - 1
     for bk, bi in blocks:
         if T is None:
             pred = np.ones(len(bk), dtype=bool)
@@ -204,7 +209,9 @@ def deepselect(blocks, k: int, block2: int, bits: int):
             st.R += 1
             ck, ci, T = radix_select_topk(ck, ci, k, bits)
             st.thresholds.append(T)
+            st.selected = True
     st.W += len(ck)
+    st.selected |= len(ck) > k
     ck, ci, kth = radix_select_topk(ck, ci, k, bits)
     return ck, ci, kth, st
 
@@ -257,10 +264,14 @@ def row_topk(x_row: np.ndarray, k: int, block: int, block2: int, seed: int = 0, 
             blocks.append((keys[lo:hi], np.arange(lo, hi, dtype=np.int64)))
         ck, ci, kth, st = deepselect(blocks, k, block2, bits)
         total.add(st)
-        parts.append((ck, ci))
+        parts.append((ck, ci, kth if len(ck) == k and st.selected else None))
     if split > 1:
+        # the k-th largest of any k elements of the row is at most the row's,
+        # so the merge admits only results at or above the largest k-th of the
+        # parts that hold k (those where a select ran and set T)
+        t0 = max([t for _, _, t in parts if t is not None], default=None)
         order = block_order(seed, row, 1, np.arange(split))
-        ck, ci, kth, st = deepselect([parts[int(p)] for p in order], k, block2, bits)
+        ck, ci, kth, st = deepselect([parts[int(p)][:2] for p in order], k, block2, bits, t0)
         total.add(st)
     vals = raw[ci]
     return RowResult(vals=vals, idx=ci, kth=kth, stats=total, reads=reads)

@@ -127,10 +127,12 @@ def test_split_plan_is_valid(name):
     L = w.k + w.block + w.block2 - 1
     assert L * (w.elem_bytes + 4) <= lds <= 160 * 1024
     # small batches are split towards one part per compute unit, within the
-    # planner's caps (balance of bytes to results, four 8-block steps per part,
-    # at most 16 parts)
+    # planner's caps (balance of bytes to results, four 8-block steps per part
+    # or two for batches under a sixteenth of the units, at most 64 parts)
     if w.batch <= 128:
-        cap = min(math.floor(math.sqrt(w.n * w.elem_bytes / (8 * w.k))), max(1, -(-w.n // w.block) // 32), 16)
+        min_blocks = 16 if w.batch * 16 <= 256 else 32
+        cap = min(math.floor(math.sqrt(w.n * w.elem_bytes / (2 * w.k))), max(1, -(-w.n // w.block) // min_blocks),
+                  64)
         assert S == max(1, min(-(-256 // w.batch), cap))
 
 
@@ -139,7 +141,7 @@ def test_split_plan_examples():
     assert ds.deepselect_plan_split(ds.DS_F32, 64, 32768, 512, 1024, 1024, 256) == 1
     assert ds.deepselect_plan_split(ds.DS_F32, 256, 151936, 64, 1024, 1024, 256) == 1
     assert ds.deepselect_plan_split(ds.DS_F32, 32, 1 << 20, 512, 1024, 1024, 256) == 8
-    assert ds.deepselect_plan_split(ds.DS_F32, 1, 1 << 20, 512, 1024, 1024, 256) == 16
+    assert ds.deepselect_plan_split(ds.DS_F32, 1, 1 << 20, 512, 1024, 1024, 256) == 64
     assert ds.deepselect_plan_split(ds.DS_F32, 1, 4096, 64, 256, 256, 256) == 1
 
 

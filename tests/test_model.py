@@ -358,3 +358,35 @@ def test_split_rows_mean_w_below_their_bound():
         x = synth.generate(name, 1)
         ws = [model.row_topk(x[0], w.k, w.block, w.block2, seed=s, split=split).stats.W for s in range(3)]
         assert np.mean(ws) <= model.expected_w_bound_row(w.n, w.k, w.block, w.block2, split), name
+
+
+def test_merge_starts_below_the_largest_part_kth():
+    """Reading c12: the merge admits only part results at or above the largest
+    k-th key among the parts (no part's k-th exceeds the row's k-th)."""
+    k, b, b2 = 16, 64, 32
+    # ascending row in 4 parts: the top part holds the row's top k, every other
+    # result lies below its k-th, so the merge admits exactly k results and
+    # only runs its final select (W = k, A = k, R = 0)
+    x = np.arange(1024, dtype=np.float32)[None, :]
+    full = model.row_topk(x[0], k, b, b2, seed=3, split=4)
+    keys = oracle.keys(x[0])
+    parts = 0
+    for lo, hi in model.part_bounds(16, 4):  # each part on its own blocks, in the row's order
+        blocks = [(keys[i * b:(i + 1) * b], np.arange(i * b, (i + 1) * b))
+                  for i in model.block_order(3, 0, 0, np.arange(lo, hi))]
+        parts += model.deepselect(blocks, k, b2, 32)[3].W
+    o_vals, o_idx = oracle.topk(x, k)
+    assert sorted(full.idx.tolist()) == sorted(o_idx[0].tolist())
+    assert full.stats.W - parts == k
+    # the merge on its own: blocks of part results with t0 = the largest k-th
+    blocks = [(np.arange(100, 116, dtype=np.uint32), np.arange(16)),
+              (np.arange(300, 316, dtype=np.uint32), np.arange(16, 32)),
+              (np.arange(200, 216, dtype=np.uint32), np.arange(32, 48))]
+    ck, ci, kth, st = model.deepselect(blocks, k, b2, 32, t0=300)
+    assert st.A == 16 and st.R == 0 and st.W == 16 and kth == 300
+    assert sorted(ck.tolist()) == list(range(300, 316))
+    # ties at t0 are admitted (>=): every result equal
+    eq = [(np.full(16, 7, dtype=np.uint32), np.arange(16 * i, 16 * i + 16)) for i in range(3)]
+    ck, ci, kth, st = model.deepselect(eq, k, b2, 32, t0=7)
+    assert st.A == 48 and kth == 7 and len(ck) == k
+    assert st.W == st.A + k * st.R

@@ -99,9 +99,10 @@ struct RunState {
         pt[cat] += now - pt_last;
         pt_last = now;
     }
-    __device__ void prof_flush() {
-        if ((threadIdx.x & 63) == 0 && blockIdx.x < (unsigned)kProfGroups) {
-            unsigned long long* o = ds_prof + ((size_t)blockIdx.x * kProfWaves + (threadIdx.x >> 6)) * kProfCats;
+    __device__ void prof_flush(unsigned group0 = 0) {
+        if ((threadIdx.x & 63) == 0 && group0 + blockIdx.x < (unsigned)kProfGroups) {
+            unsigned long long* o =
+                ds_prof + ((size_t)(group0 + blockIdx.x) * kProfWaves + (threadIdx.x >> 6)) * kProfCats;
             for (int i = 0; i < kProfCats; ++i) atomicAdd(&o[i], (unsigned long long)pt[i]);
         }
     }
@@ -115,7 +116,6 @@ struct RunState {
     uint32_t kmax = 0;  // the largest key this lane appended (reduced over the wave at a select)
     bool fset = false;  // a threshold filters the blocks (T, or one shared by another part)
     uint32_t fkey = 0;  // its key: the larger of T and the shared one
-    uint32_t lo0 = 0;   // before T is set: a key the row's k-th is known to reach (0: none)
 };
 
 template <class D>
@@ -171,7 +171,7 @@ __device__ __forceinline__ void publish_max(RunState& st, uint32_t kmax) {
 template <class D, int NW>
 __device__ __forceinline__ void select_buffer(Lds<D>& s, RunState& st, uint32_t k) {
     static_assert(NW <= 8, "one largest-key cell per wave in misc[8..16)");
-    const uint32_t lo = st.tset ? st.tkey : st.lo0;
+    const uint32_t lo = st.tset ? st.tkey : 0u;
     const uint32_t wmax = wave_max(st.kmax);
     if (lane_id() == 0) s.misc[8 + wave_id()] = wmax;
     lds_barrier();  // appends and the waves' largest keys are visible
@@ -183,7 +183,7 @@ __device__ __forceinline__ void select_buffer(Lds<D>& s, RunState& st, uint32_t 
     }
     hi = uniform(hi);
     st.tkey = select_topk<D, NW>(s.keys, s.idx, s.hist, s.fold, s.tot, s.gathered, s.misc + 2, s.junk, st.len, k, lo,
-                                  hi > lo ? hi : lo, st.tset || lo == 0u);
+                                  hi > lo ? hi : lo);
     st.tset = true;
     st.fkey = st.fset && st.fkey > st.tkey ? st.fkey : st.tkey;
     st.fset = true;
@@ -1717,19 +1717,192 @@ __device__ __forceinline__ void load_part_tile(MergeTile& t, const Params& p, in
         const int64_t m = p.lengths ? ceil_div(row_len(p, row), (int64_t)p.B) : p.m;
         col0 = (uint32_t)(part_begin(m, part, p.split) * p.B);
     }
+    // unconditional loads at an index clamped into the part's slots (a
+    // conditional load would be waited for before the next is issued)
+    uint32_t w[kMT], c[kMT];
+#pragma unroll
+    for (int q = 0; q < kMT; ++q) {
+        const uint32_t e = (uint32_t)q * NW * 64 + (uint32_t)threadIdx.x;
+        const int64_t at = off + (t0 + e < k ? e : k - 1u - t0);
+        w[q] = p.ws_keys[at];
+        if constexpr (!kPkParts) c[q] = p.ws_idx[at];
+    }
 #pragma unroll
     for (int q = 0; q < kMT; ++q) {
         const uint32_t e = (uint32_t)q * NW * 64 + (uint32_t)threadIdx.x;
         const bool inb = t0 + e < k;
         if constexpr (kPkParts) {
-            const uint32_t w = inb ? p.ws_keys[off + e] : 0u;
-            t.key[q] = w >> 16;
-            t.col[q] = col0 + (w & 0xFFFFu);
+            t.key[q] = inb ? w[q] >> 16 : 0u;
+            t.col[q] = col0 + (w[q] & 0xFFFFu);
         } else {
-            t.key[q] = inb ? p.ws_keys[off + e] : 0u;
-            t.col[q] = inb ? p.ws_idx[off + e] : 0u;
+            t.key[q] = inb ? w[q] : 0u;
+            t.col[q] = inb ? c[q] : 0u;
         }
     }
+}
+
+// A part's results for the merge, read kBC per lane at a time with every
+// load of a chunk issued before any is used: key and column of results
+// e0 + j*64 + lane (j < kBC) of part `part`, zero past cnt.
+constexpr int kBC = 8;
+template <bool kPkParts>
+struct PartChunk {
+    uint32_t key[kBC], col[kBC];
+    // The loads are unconditional, at an index clamped into the part's k
+    // slots (in bounds whatever the count), and the values past cnt are
+    // zeroed after: a conditional load would make the compiler wait for each
+    // one before issuing the next.
+    // keys only (the counting pass)
+    __device__ __forceinline__ void load_keys(const Params& p, int64_t row, int64_t part, uint32_t e0, uint32_t cnt) {
+        const uint32_t* base = p.ws_keys + (row * p.split + part) * (int64_t)p.k;
+        const uint32_t lane = (uint32_t)lane_id(), last = (uint32_t)p.k - 1u;
+        uint32_t w[kBC];
+#pragma unroll
+        for (int j = 0; j < kBC; ++j) {
+            const uint32_t e = e0 + (uint32_t)j * 64u + lane;
+            w[j] = base[e < last ? e : last];
+        }
+#pragma unroll
+        for (int j = 0; j < kBC; ++j) {
+            const uint32_t e = e0 + (uint32_t)j * 64u + lane;
+            key[j] = e < cnt ? (kPkParts ? w[j] >> 16 : w[j]) : 0u;
+        }
+    }
+    __device__ __forceinline__ void load(const Params& p, int64_t row, int64_t part, uint32_t e0, uint32_t cnt) {
+        const int64_t off = (row * p.split + part) * (int64_t)p.k;
+        uint32_t col0 = 0;
+        if constexpr (kPkParts) {
+            const int64_t m = p.lengths ? ceil_div(row_len(p, row), (int64_t)p.B) : p.m;
+            col0 = (uint32_t)(part_begin(m, part, p.split) * p.B);
+        }
+        const uint32_t lane = (uint32_t)lane_id(), last = (uint32_t)p.k - 1u;
+        uint32_t w[kBC], c[kBC];
+#pragma unroll
+        for (int j = 0; j < kBC; ++j) {
+            const uint32_t e = e0 + (uint32_t)j * 64u + lane;
+            const uint32_t ec = e < last ? e : last;
+            w[j] = p.ws_keys[off + ec];
+            if constexpr (!kPkParts) c[j] = p.ws_idx[off + ec];
+        }
+#pragma unroll
+        for (int j = 0; j < kBC; ++j) {
+            const uint32_t e = e0 + (uint32_t)j * 64u + lane;
+            const bool in = e < cnt;
+            if constexpr (kPkParts) {
+                key[j] = in ? w[j] >> 16 : 0u;
+                col[j] = col0 + (w[j] & 0xFFFFu);
+            } else {
+                key[j] = in ? w[j] : 0u;
+                col[j] = in ? c[j] : 0u;
+            }
+        }
+    }
+};
+
+// The merge's parts in order up to the first compaction, all at once. Until
+// then T stays where it started, so every part's admitted results can be
+// counted in parallel (wave w takes order positions w, w + NW, ...); a
+// prefix sum over the order gives each part's place in the buffer and the
+// first part after which the buffer holds k + B2 or more. The parts up to
+// and including that one are appended in parallel: the buffer, A and max_len
+// end exactly as the part-by-part loop leaves them. Returns that part's
+// order position, or S when no part reaches it. cnt_of(part): the part's
+// number of results.
+template <class D, int NW, bool kPkParts, class CntOf>
+__device__ __forceinline__ int32_t merge_bulk(Lds<D>& s, RunState& st, const Params& p, int64_t row, uint32_t* pcnt,
+                                              CntOf&& cnt_of) {
+    const int32_t S = p.split;
+    const uint32_t k = (uint32_t)p.k, B2 = (uint32_t)p.B2;
+    const int w = wave_id(), lane = lane_id();
+    const bool filt = st.tset;
+    const uint32_t thr = st.tkey;
+    // the wave's parts kBP at a time, their loads issued together
+    constexpr int kBP = 4;
+    for (int32_t i0 = w; i0 < S; i0 += NW * kBP) {
+        int64_t part[kBP];
+        uint32_t cnt[kBP], c[kBP], most = 0;
+#pragma unroll
+        for (int b = 0; b < kBP; ++b) {
+            const int32_t i = i0 + b * NW;
+            part[b] = i < S ? (int64_t)uniform(s.perm[i]) : 0;
+            cnt[b] = i < S ? cnt_of(part[b]) : 0u;
+            c[b] = 0;
+            most = cnt[b] > most ? cnt[b] : most;
+        }
+        for (uint32_t e0 = 0; e0 < most; e0 += 64 * kBC) {
+            PartChunk<kPkParts> pc[kBP];
+#pragma unroll
+            for (int b = 0; b < kBP; ++b) pc[b].load_keys(p, row, part[b], e0, cnt[b]);
+#pragma unroll
+            for (int b = 0; b < kBP; ++b) {
+#pragma unroll
+                for (int j = 0; j < kBC; ++j)
+                    c[b] += e0 + (uint32_t)j * 64u + (uint32_t)lane < cnt[b] && (!filt || pc[b].key[j] > thr) ? 1u : 0u;
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kBP; ++b) {
+            const uint32_t t = wave_prefix_sum(c[b]);
+            if (lane == 63 && i0 + b * NW < S) pcnt[i0 + b * NW] = t;
+        }
+    }
+    lds_barrier();
+    // wave 0: the exclusive prefix over the order in place, and the trigger
+    if (w == 0) {
+        uint32_t carry = st.len, end = 0;
+        int32_t trig = S;
+        for (int32_t i0 = 0; i0 < S; i0 += 64) {
+            const int32_t i = i0 + lane;
+            const uint32_t c = i < S ? pcnt[i] : 0u;
+            const uint32_t incl = wave_prefix_sum(c);
+            const uint64_t over = __ballot(i < S && carry + incl >= k + B2);
+            if (i < S) pcnt[i] = carry + incl - c;
+            if (trig == S && over != 0ull) {
+                const int L = __builtin_ctzll(over);
+                trig = i0 + L;
+                end = carry + uniform(__builtin_amdgcn_readlane(incl, L));
+            }
+            carry += uniform(__builtin_amdgcn_readlane(incl, 63));
+        }
+        if (lane == 0) {
+            s.misc[3] = (uint32_t)trig;
+            s.misc[4] = trig == S ? carry : end;
+        }
+    }
+    lds_barrier();
+    const int32_t trig = (int32_t)uniform(s.misc[3]);
+    const int32_t last = trig < S ? trig : S - 1;
+    const uint32_t end = uniform(s.misc[4]);  // the length after the last part appended here
+    uint32_t kmax = 0;
+    for (int32_t i = w; i <= last; i += NW) {
+        // a part that admits nothing is skipped (its count is the gap to the next place)
+        uint32_t at = uniform(pcnt[i]);
+        const uint32_t next = i < last ? uniform(pcnt[i + 1]) : end;
+        if (next == at) continue;
+        const int64_t part = (int64_t)uniform(s.perm[i]);
+        const uint32_t cnt = cnt_of(part);
+        for (uint32_t e0 = 0; e0 < cnt; e0 += 64 * kBC) {
+            PartChunk<kPkParts> pc;
+            pc.load(p, row, part, e0, cnt);
+#pragma unroll
+            for (int j = 0; j < kBC; ++j) {
+                const bool pred = e0 + (uint32_t)j * 64u + (uint32_t)lane < cnt && (!filt || pc.key[j] > thr);
+                const uint64_t m = __ballot(pred);
+                if (pred) {
+                    const uint32_t pos = at + lanes_below(m);
+                    s.keys[pos] = (typename D::Key)pc.key[j];
+                    s.idx[pos] = pc.col[j];
+                    kmax = pc.key[j] > kmax ? pc.key[j] : kmax;
+                }
+                at += (uint32_t)__popcll(m);
+            }
+        }
+    }
+    publish_max(st, kmax);
+    st.A += end - st.len;
+    st.len = end;
+    st.maxlen = end > st.maxlen ? end : st.maxlen;
+    return trig;
 }
 
 // Tile number `tile` of the merge: tile tile % tpp of the part at order
@@ -1753,6 +1926,7 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
     // with two tiles in all (two parts of one tile each: k <= NW*256), both
     // are loaded before the order is built, which hides their latency
     const bool both = tiles == 2 && tpp == 1;
+    uint32_t* pcnt = reinterpret_cast<uint32_t*>(smem + p.L.pcnt);
     for (int64_t row = blockIdx.x; row < p.batch; row += gridDim.x) {
         MergeTile cur, nxt, pre0, pre1;
         if (both) {
@@ -1763,14 +1937,27 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
         // part q's, loaded with the first tiles (more than 64 parts: read
         // where needed)
         const bool counted = p.lengths || p.ws_share;
-        uint32_t part_cnt = k, part_t = 0;
+        uint32_t part_cnt = k;
         if (counted && S <= 64 && lane_id() < S) part_cnt = p.ws_cnt[row * S + lane_id()];
-        if (S <= 64 && lane_id() < S) part_t = p.ws_tkey[row * S + lane_id()];
+        // the largest k-th key of the parts that hold k results: the k-th of
+        // any k elements of the row is at most the row's, so the merge admits
+        // only results at or above it (T starts just below it)
+        uint32_t t0 = 0;
+        for (int32_t q = lane_id(); q < S; q += 64) {
+            const uint32_t t = p.ws_tkey[row * S + q];
+            t0 = t > t0 ? t : t0;
+        }
+        t0 = wave_max(t0);
         // the previous row's final select has ended, so the histogram and the
         // largest-key cell are free to clear before the barrier that frees LDS
         begin_item<D, NW>(s);
         lds_barrier();
         RunState st;
+        DS_PROF(st, 0);
+        if (t0 != 0u) {
+            st.tset = st.fset = true;
+            st.tkey = st.fkey = t0 - 1u;
+        }
         bool swap = false;
 
         if (both) {
@@ -1781,11 +1968,20 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
             swap = splitmix_at(p.seed, ctr0 + 1u) < splitmix_at(p.seed, ctr0);
             cur = swap ? pre1 : pre0;
             nxt = swap ? pre0 : pre1;
-        } else {
-            build_order<NW>(s.perm, p.seed, row, 1, 0, S, s.base);
-            load_merge_tile<NW, kPkParts>(cur, p, s.perm, row, 0, tpp);
         }
-        for (int64_t j = 0; j < tiles; ++j) {
+        int64_t j0 = 0;  // the first tile the part-by-part loop takes
+        if (!both) {
+            build_order<NW>(s.perm, p.seed, row, 1, 0, S, s.base);
+            DS_PROF(st, 1);
+            const int32_t trig = merge_bulk<D, NW, kPkParts>(s, st, p, row, pcnt, [&](int64_t part) -> uint32_t {
+                return counted ? uniform(p.ws_cnt[row * S + part]) : k;
+            });
+            DS_PROF(st, 2);
+            if (trig < S) compact<D, NW>(s, st, k);
+            j0 = (int64_t)(trig + 1) * tpp;
+            if (j0 < tiles) load_merge_tile<NW, kPkParts>(cur, p, s.perm, row, j0, tpp);
+        }
+        for (int64_t j = j0; j < tiles; ++j) {
             if (!both && j + 1 < tiles) load_merge_tile<NW, kPkParts>(nxt, p, s.perm, row, j + 1, tpp);
             const uint32_t t0 = (uint32_t)(j % tpp) * TE;
             // results of the part: k, or fewer for a part shorter than k or
@@ -1831,30 +2027,44 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
             }
             publish_max(st, kmax);
             if ((j + 1) % tpp == 0) {  // a part's block ends: the compaction check
-                // an appended part's k-th key is at most the buffer's k-th
-                // from now on: the largest so far bounds the merge's select
-                // from below (a part with fewer than k results gives none)
-                if (S <= 64) {
-                    const int64_t i = j / tpp;
-                    const int64_t part = both ? (swap ? 1 - i : i) : (int64_t)uniform(s.perm[i]);
-                    const uint32_t t = uniform(__builtin_amdgcn_readlane(part_t, (int)part));
-                    st.lo0 = t > st.lo0 ? t : st.lo0;
-                }
                 st.maxlen = st.len > st.maxlen ? st.len : st.maxlen;
                 if (st.len >= k + B2) compact<D, NW>(s, st, k);
             }
             cur = nxt;
         }
+        DS_PROF(st, 3);
         final_select<D, NW>(s, st, k);
-        uint64_t W = st.W, A = st.A, R = st.R, maxlen = st.maxlen;
-        for (int32_t q = 0; q < S; ++q) {
-            const uint64_t* o = p.ws_stats + (row * S + q) * DS_STATS_PER_ROW;
-            W += o[DS_STAT_W];
-            A += o[DS_STAT_A];
-            R += o[DS_STAT_R];
-            maxlen = o[DS_STAT_MAX_LEN] > maxlen ? o[DS_STAT_MAX_LEN] : maxlen;
+        DS_PROF(st, 4);
+        // the parts' statistics: lane q takes parts q, q + 64, ..., then the
+        // wave adds them up (only when asked for)
+        uint64_t W = 0, A = 0, R = 0, maxlen = 0;
+        if (p.stats) {
+            for (int32_t q = lane_id(); q < S; q += 64) {
+                const uint64_t* o = p.ws_stats + (row * S + q) * DS_STATS_PER_ROW;
+                W += o[DS_STAT_W];
+                A += o[DS_STAT_A];
+                R += o[DS_STAT_R];
+                maxlen = o[DS_STAT_MAX_LEN] > maxlen ? o[DS_STAT_MAX_LEN] : maxlen;
+            }
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                W += __shfl_xor(W, d);
+                A += __shfl_xor(A, d);
+                R += __shfl_xor(R, d);
+                const uint64_t m = __shfl_xor(maxlen, d);
+                maxlen = m > maxlen ? m : maxlen;
+            }
         }
+        W += st.W;
+        A += st.A;
+        R += st.R;
+        maxlen = st.maxlen > maxlen ? st.maxlen : maxlen;
+        DS_PROF(st, 5);
         write_row<D, NW>(s, p, row, st.len, W, A, R, maxlen);
+        DS_PROF(st, 6);
+#ifdef DS_PROFILE
+        st.prof_flush(2048);
+#endif
     }
 }
 
@@ -1921,16 +2131,18 @@ static bool lds_fits(int dtype, int64_t n, int64_t k, int64_t B, int64_t B2, int
 static int plan_split(int dtype, int64_t batch, int64_t n, int32_t k, int32_t B, int32_t B2, int32_t num_cus) {
     const int64_t lo = split_lower_bound(dtype, n, B);
     // Split when the rows fill at most half the compute units, about one
-    // part per unit; no more parts than keep the streamed bytes of a part
-    // ahead of its k results (sqrt(N*size / 8k)), no part shorter than four
-    // steps of 8 blocks (the merge's cost outweighs shorter parts), and at
-    // most kSplitPlanMax parts (the merge grows with their number).
-    constexpr int64_t kSplitPlanMax = 16;
+    // part per unit; no more parts than balance a part's streamed bytes with
+    // the merge's S*k results (sqrt(N*size / 2k)); no part shorter than four
+    // steps of 8 blocks, or two when the batch fills under a sixteenth of the
+    // units (a part's fixed costs outweigh shorter ones); at most
+    // kSplitPlanMax parts.
+    constexpr int64_t kSplitPlanMax = 64;
     int64_t S = 1;
     if (batch > 0 && batch <= num_cus / 2) S = ceil_div(num_cus, batch);
-    const double bal = std::floor(std::sqrt((double)n * elem_bytes(dtype) / (8.0 * (double)k)));
+    const double bal = std::floor(std::sqrt((double)n * elem_bytes(dtype) / (2.0 * (double)k)));
     S = std::min<int64_t>(S, std::max<int64_t>(1, (int64_t)bal));
-    S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(n, B) / 32));
+    const int64_t min_blocks = batch * 16 <= num_cus ? 16 : 32;
+    S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(n, B) / min_blocks));
     S = std::min<int64_t>(S, kSplitPlanMax);
     S = std::max<int64_t>(S, lo);
     while (S > lo && (!split_ok(n, k, B, S) || !lds_fits(dtype, n, k, B, B2, S, kGW))) --S;
@@ -2064,12 +2276,13 @@ static int launch_all(KernelKind kind, int units, int waves, bool vec, Params pr
     }
     if (rc != DS_OK || prm.split == 1) return rc;
     // the merge runs on 8 waves when a part's k results need more than one
-    // tile of 4 waves and the layout fits, else on 4 (measured: 8 waves are
-    // 2 us faster at k = 2048, 4 waves 1 to 3.6 us faster at k = 512)
+    // tile of 4 waves, or when 16 parts or more are counted at its start, and
+    // the layout fits, else on 4 (measured: 8 waves are 2 us faster at
+    // k = 2048, 4 waves 1 to 3.6 us faster at k = 512 with 8 parts)
     const int dtype = DM::kBytes == 4 ? DS_F32 : DS_BF16;
     Layout M8 = make_merge_layout(dtype, prm.k, prm.B2, prm.split, 8);
     if (prm.sorted) M8 = with_sort(M8, prm.k);
-    if (prm.k > kGW * 64 * kMT && M8.total <= kLdsLimit) {
+    if ((prm.k > kGW * 64 * kMT || prm.split >= 16) && M8.total <= kLdsLimit) {
         prm.L = M8;
         return launch_kernel(deepselect_merge_kernel<DM, 8, is_packed<D>::value>, prm.batch, 8 * 64, prm.L.total,
                              st, prm);

@@ -65,6 +65,7 @@ struct Layout {
     uint32_t misc;   // 16 uint32 of broadcast scratch
     uint32_t ring;   // streaming ring: waves x ring_depth blocks of ring_units KiB (0 if none)
     uint32_t sort;   // sorted output: next_pow2(k) uint64 sort words (0 if not asked for)
+    uint32_t pcnt;   // merge: one count per part (0 if none)
     uint32_t total;  // bytes
     int32_t cap;     // candidate buffer capacity in entries
     int32_t junk;    // first junk entry (cap padded to 8)
@@ -158,8 +159,12 @@ inline Layout with_sort(Layout L, int64_t k) {
 }
 
 // Layout of the merge kernel of split rows: S blocks of k candidates.
+// The merge also keeps one count per part (uint32, in `pcnt`).
 inline Layout make_merge_layout(int dtype, int64_t k, int64_t B2, int64_t S, int waves) {
-    return make_layout_raw(elem_bytes(dtype), capacity(k, k, B2), S, waves);
+    Layout L = make_layout_raw(elem_bytes(dtype), capacity(k, k, B2), S, waves);
+    L.pcnt = (uint32_t)align_up(L.total, 16);
+    L.total = (uint32_t)align_up(L.pcnt + (size_t)S * 4, 16);
+    return L;
 }
 
 // Workspace of split rows (device memory): every part's k (key, column) pairs
