@@ -2141,7 +2141,7 @@ static int plan_split(int dtype, int64_t batch, int64_t n, int32_t k, int32_t B,
     if (batch > 0 && batch <= num_cus / 2) S = ceil_div(num_cus, batch);
     const double bal = std::floor(std::sqrt((double)n * elem_bytes(dtype) / (2.0 * (double)k)));
     S = std::min<int64_t>(S, std::max<int64_t>(1, (int64_t)bal));
-    const int64_t min_blocks = batch * 16 <= num_cus ? 16 : 32;
+    const int64_t min_blocks = batch <= num_cus / 16 ? 16 : 32;
     S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(n, B) / min_blocks));
     S = std::min<int64_t>(S, kSplitPlanMax);
     S = std::max<int64_t>(S, lo);
