@@ -300,7 +300,7 @@ def main() -> int:
     st_dev = torch.empty((w.batch, 4), dtype=torch.int64, device=dev)
     opt_st = ds.DsOptions(int(split), int(args.waves), st_dev.data_ptr(), None, 0, int(args.kernel),
                           int(args.sorted), lens.data_ptr() if lens is not None else None, None, 1.0, 1.0, None,
-                          None, 0)
+                          None, int(args.share))
     rc = fn(ptrs[0], dt, w.batch, w.n, w.n, w.k, w.block, w.block2, seed, vptr, iptr, sptr, ctypes.byref(opt_st))
     if rc != 0:
         raise RuntimeError(f"deepselect_topk_ex failed: {ds.deepselect_status_string(rc)}")

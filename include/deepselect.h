@@ -155,12 +155,24 @@ typedef struct ds_options {
     const float *sample_u;
     int32_t *sample_idx;
     /* Split rows: 1 = the parts of a row share their thresholds (0 = off;
-     * other values DS_ERR_BLOCK). After each compaction a part publishes its
-     * T, and the streaming (ring) kernel filters its next blocks with the
-     * largest T any part of the row has published so far. Any part's k-th
-     * value is at most the row's, so the result set is the same; the
-     * statistics then depend on timing (W = A + k*R still holds per row).
-     * Adds one small kernel (clearing the row cells) before the parts. */
+     * other values DS_ERR_BLOCK). In the streaming (ring) kernel a part
+     * publishes its T (an atomic maximum on the row's cell) at the start of
+     * the step after a compaction raised it above what the cell held, one
+     * wave per part copies the cell each step, and from two steps later the
+     * part filters its blocks with that key when it is above its own T. Its
+     * final select first drops the entries at or below such a key. Any
+     * part's k-th value is at most the row's, so the result set is the same;
+     * the statistics then depend on timing (W = A + k*R still holds per row,
+     * W counting the whole buffer at the final stage).
+     * The row cells (one uint64 per row, 128 bytes apart) must be zero when
+     * the parts start, and the merge kernel leaves them zero. The first 1024
+     * cells sit at the start of a library-owned workspace or of the noalloc
+     * scratch, where no other array overlaps them, so they are cleared only
+     * once: by the first such call that is not under graph capture. Cells
+     * beyond 1024 rows, every cell of a caller workspace, and the reserved
+     * cells of a call made under capture before that are cleared by one
+     * small kernel before the parts. After a launch that fails, the next
+     * call clears them again. */
     int32_t share_threshold;
 } ds_options_t;
 
@@ -186,9 +198,10 @@ int deepselect_topk_ex(const void *x, int dtype, int64_t batch, int64_t N, int64
  * hipMalloc. It calls no hipMalloc, hipFree or other allocating routine. The
  * workspace of split rows (every part's results, counts, k-th keys,
  * statistics and shared-threshold cells) lives in a static device array of
- * deepselect_scratch_bytes() bytes (8 MiB), one copy per GPU the library runs
- * on, kept until the process ends; its device address is looked up once per
- * device on the first call there. Arguments and results are those of
+ * 8 MiB, one copy per GPU the library runs on, kept until the process ends;
+ * its device address is looked up once per device on the first call there.
+ * Its first 128 KiB hold 1024 reserved shared-threshold cells (see
+ * share_threshold); deepselect_scratch_bytes() is the rest. Arguments and results are those of
  * deepselect_topk_ex with the same options, except:
  *   - opt->workspace must be NULL (else DS_ERR_SCRATCH);
  *   - a call whose split needs more workspace than the scratch holds
@@ -196,15 +209,18 @@ int deepselect_topk_ex(const void *x, int dtype, int64_t batch, int64_t N, int64
  *     DS_ERR_SCRATCH with nothing enqueued; force a smaller opt->split or use
  *     deepselect_topk_ex.
  * Every call on one GPU shares that GPU's scratch, which keeps the last
- * call's contents (a call needs none from before it: the cells that must
- * start at zero are cleared by a kernel of the call itself). Calls that may
- * overlap on one GPU (other streams, other threads) race on it: order them.
+ * call's contents. A call needs none of them except the reserved cells, which
+ * every call leaves zero (share_threshold says when they are cleared). Calls
+ * that may overlap on one GPU (other streams, other threads) race on it:
+ * order them.
  * Calls with one part per row use no scratch. */
 int deepselect_topk_noalloc(const void *x, int dtype, int64_t batch, int64_t N, int64_t row_stride,
                             int32_t k, int32_t B, int32_t B2, uint64_t seed, void *out_vals,
                             int32_t *out_idx, void *stream, const ds_options_t *opt);
 
-/* Bytes of the static scratch deepselect_topk_noalloc uses on each GPU. */
+/* Bytes of the static scratch deepselect_topk_noalloc has for the workspace
+ * of a call on each GPU (8 MiB less its 128 KiB of reserved cells): a call fits
+ * when deepselect_workspace_bytes for its shape is at most this. */
 size_t deepselect_scratch_bytes(void);
 
 /* The split factor the library picks for this shape on a device with num_cus

@@ -663,6 +663,49 @@ def test_shared_threshold(case):
         check_rows(x, raw_of(again[0]), again[1].cpu().numpy(), w.k)
 
 
+def check_topk_values(x, vals, idx, k):
+    """Row by row: the k values are the k largest of the row as a multiset
+    (np.partition), each index points at its value, no index repeats."""
+    v = vals.view(np.float32)
+    top = -np.sort(np.partition(-x, k - 1, axis=1)[:, :k], axis=1)
+    assert np.array_equal(-np.sort(-v, axis=1), top)
+    assert np.array_equal(np.take_along_axis(x, idx.astype(np.int64), axis=1), v)
+    srt = np.sort(idx, axis=1)
+    assert np.all(srt[:, 1:] != srt[:, :-1])
+
+
+def test_shared_cells_left_zero():
+    # the merge leaves every row cell zero and the library workspace's
+    # reserved cells are cleared once, so a call on much smaller values right
+    # after one on larger values must not be filtered by the earlier
+    # thresholds (batches below and above the 1024 reserved cells, calls
+    # without sharing in between). Rows ascend, so the upper part's threshold
+    # stops the lower part once it arrives: the admissions over the sequence
+    # show that the sharing path ran. (65536 columns in blocks of 512, two
+    # parts: 8 ring steps per wave, or 16 on the 1100-row calls.)
+    n, k, B, B2, S = 65536, 64, 512, 512, 2
+    seq = [(3, 1000.0, True), (5, 0.0, True), (1, 5000.0, False), (1100, 2000.0, True), (1100, -10.0, True),
+           (2, -3000.0, True), (6, -4000.0, True)]
+    a_plain = a_shared = 0
+    for rows, shift, share in seq:
+        log(f"[gpu] shared cells: rows {rows} shift {shift} share {share}")
+        ramp = np.float32(shift) + np.arange(n, dtype=np.float32) * np.float32(100.0 / n)
+        x = np.tile(ramp, (rows, 1))
+        xt = to_device(x)
+        if share:
+            _, _, st0 = ds.topk(xt, k, B, B2, 11, split=S, stats=True)
+        v, i, st = ds.topk(xt, k, B, B2, 11, split=S, stats=True, share_threshold=share)
+        torch.cuda.synchronize()
+        check_topk_values(x, raw_of(v), i.cpu().numpy(), k)
+        st = st.cpu().numpy()
+        assert np.all(st[:, 0] == st[:, 1] + k * st[:, 2]), "W = A + k R"
+        if share:
+            a_plain += int(st0.cpu().numpy()[:, 1].sum())
+            a_shared += int(st[:, 1].sum())
+    log(f"[gpu]   admitted over the shared calls: {a_plain} plain, {a_shared} shared")
+    assert a_shared < a_plain, "the parts did not share thresholds"
+
+
 # ---------------------------------------------------------------- randomised parity
 
 def draw_case(i):

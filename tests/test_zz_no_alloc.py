@@ -99,6 +99,27 @@ def test_noalloc_matches_the_allocating_call_twice():
             assert np.array_equal(got[2], ref[2])
 
 
+def test_noalloc_shared_cells_left_zero():
+    # the scratch's reserved threshold cells stay zero from call to call: a
+    # call on much smaller values right after one on larger values (batches
+    # below and above the 1024 reserved cells) gets the same result set as the
+    # allocating call
+    rng = np.random.default_rng(32)
+    n, k, B, S = 65536, 16, 512, 2  # 8 or 16 ring steps per wave: the parts share thresholds
+    for rows, shift in [(3, 1000.0), (5, 0.0), (1100, 2000.0), (1100, -10.0), (2, -3000.0)]:
+        log(f"[gpu] no-alloc shared cells: rows {rows} shift {shift}")
+        x = (rng.random((rows, n), dtype=np.float32) * np.float32(100.0) + np.float32(shift)).astype(np.float32)
+        xt = to_device(x)
+        ref = run(ds.deepselect_topk_ex, xt, k, B, B, 5, S, 1)
+        got = run(ds.deepselect_topk_noalloc, xt, k, B, B, 5, S, 1)
+        top = -np.sort(np.partition(-x, k - 1, axis=1)[:, :k], axis=1)
+        for vals, idx, st in (ref, got):
+            v = vals.view(np.float32)
+            assert np.array_equal(-np.sort(-v, axis=1), top)
+            assert np.array_equal(np.take_along_axis(x, idx.astype(np.int64), axis=1), v)
+            assert np.all(st[:, 0] == st[:, 1] + k * st[:, 2])
+
+
 def test_noalloc_refuses_a_workspace_beyond_the_scratch():
     # 4096 rows of 4096 bfloat16 split 4 ways at k = 512 need 64 MiB of part results
     batch, n, k, B = 4096, 4096, 512, 512

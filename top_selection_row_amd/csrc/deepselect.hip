@@ -42,6 +42,7 @@
 #include <string.h>
 
 #include <map>
+#include <atomic>
 #include <mutex>
 #include <thread>
 #include <tuple>
@@ -55,6 +56,8 @@ namespace ds {
 
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every part (parts < 2 GiB)
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
+constexpr int kAgentCoherent = 16;  // buffer load cache policy: coherent at device scope
+constexpr int64_t kShareMinSteps = 6;  // ring steps per wave below which threshold sharing is off
 
 struct Params {
     const void* x;
@@ -128,7 +131,9 @@ struct Lds {
     uint32_t* gathered;
     uint32_t* cnt;
     uint16_t* perm;
-    uint32_t* misc;  // [2] gathered-key counter, [8 + w] wave w's largest appended key
+    uint32_t* misc;  // [2] gathered-key counter, [8 + w] wave w's largest appended key,
+                     // [16, 32) four copies of the row's shared threshold cell
+                     // (16 bytes each, the cell in the first 8)
     unsigned char* base;
     uint32_t junk;   // first junk entry of the candidate arrays
 };
@@ -201,9 +206,18 @@ __device__ __forceinline__ void compact(Lds<D>& s, RunState& st, uint32_t k) {
 }
 
 // Final RadixSelectTopK (its input length counts in W); ends with a barrier.
+// With drop_shared, a filter key that another part raised above this part's
+// own T first drops the entries at or below it (appended before the key was
+// known): the row's k largest are among the other part's results and this
+// part's keys above the key, so the select, if one is still needed, runs on
+// what is left (W still counts the whole buffer, so W = A + k R holds).
 template <class D, int NW>
-__device__ __forceinline__ void final_select(Lds<D>& s, RunState& st, uint32_t k) {
+__device__ __forceinline__ void final_select(Lds<D>& s, RunState& st, uint32_t k, bool drop_shared = false) {
     st.W += st.len;
+    if (drop_shared && st.len > 0u && st.fset && (!st.tset || st.fkey > st.tkey)) {
+        lds_barrier();  // the appends are visible
+        st.len = partition_keep<D, NW>(s.keys, s.idx, s.tot, st.len, st.fkey, 0u, s.junk);
+    }
     if (st.len > k) select_buffer<D, NW>(s, st, k);
     lds_barrier();
 }
@@ -887,7 +901,22 @@ struct RingStreamer {
         int32_t issued = 0;  // steps whose block of this wave is fetched
         if (nsteps > 0) fetch(w, 0), issued = 1;
         BlockRegs<U> r;
-        uint64_t shared = 0;  // the row's shared threshold cell, as read before the last refill
+        // The row's shared threshold cell: at the start of step s wave 0
+        // copies it into LDS copy s % 4 by the same kind of asynchronous load
+        // as the blocks (no register waits for it: a use of a value loaded
+        // into a register one step earlier gets a wait for every load in
+        // flight, the newest block's included). Wave 0's wait for its next
+        // block covers the copy, and that step's count exchange barrier
+        // comes after the wait, so every wave reads copy s % 4 after the
+        // appends of step s + 1 and filters with it from step s + 2: one read
+        // of the cell per workgroup and step, and the same filter key in
+        // every wave. Wave 0 rewrites the copy at step s + 4, after the
+        // barrier of step s + 2 that every wave reaches with its read done.
+        const __amdgpu_buffer_rsrc_t cell =
+            __builtin_amdgcn_make_buffer_rsrc(share, (short)0, 8, (int)kRsrcWord3);
+        const uint32_t* copies = s.misc + 16;
+        uint32_t sh_lo = 0, sh_hi = 0;  // the cell as copied two steps before this one
+        uint64_t told = 0;              // the last T this part published, + 1 (thread 0)
         for (int32_t stp = 0; stp < nsteps; ++stp) {
             const int32_t q = stp % depth;
             const int32_t nblk = ms - stp * NW < NW ? ms - stp * NW : NW;  // blocks in this step
@@ -897,11 +926,26 @@ struct RingStreamer {
             wait_block(issued - 1 - stp);
             read_slot(q, r);
             DS_PROF(st, 1);
-            if (share && shared != 0u) {
-                // another part's threshold (any part's k-th is at most the
-                // row's) raises the filter of this wave's next blocks
-                const uint32_t key = uniform((uint32_t)(shared - 1u));
-                if (!st.fset || key > st.fkey) st.fkey = key, st.fset = true;
+            if (share) {
+                const uint64_t shared = uniform(sh_lo) | ((uint64_t)uniform(sh_hi) << 32);
+                if (shared != 0u) {
+                    // another part's threshold (any part's k-th is at most
+                    // the row's) raises the filter of this wave's blocks
+                    const uint32_t key = (uint32_t)(shared - 1u);
+                    if (!st.fset || key > st.fkey) st.fkey = key, st.fset = true;
+                }
+                // The part's T goes out when it is above what the cell held,
+                // and wave 0 copies the cell: both issued here, a step's work
+                // before wave 0's next wait for a block.
+                const uint64_t mine = st.tset ? (uint64_t)st.tkey + 1u : 0u;
+                if (threadIdx.x == 0 && mine > told && mine > shared) {
+                    __hip_atomic_fetch_max(share, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    told = mine;
+                }
+                if (stp + 2 < nsteps && threadIdx.x < 2u)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        cell, (__attribute__((address_space(3))) void*)(copies + 4 * (stp & 3)), 4, threadIdx.x * 4u,
+                        0, 0, kAgentCoherent);
             }
             if (stp == 0) {
                 for (; issued < depth && issued < nsteps; ++issued) fetch(issued * NW + w, issued);
@@ -912,16 +956,17 @@ struct RingStreamer {
                 const int32_t trig = append_from(r, boff, blen, first, nblk, ring + q * U * 64);
                 if (trig < 0) break;
                 compact<D, NW>(s, st, k);
-                if (share && threadIdx.x == 0)
-                    __hip_atomic_fetch_max(share, (uint64_t)st.tkey + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (trig >= nblk - 1) break;
                 first = trig + 1;  // the blocks behind it, against the new T
             }
+            if (share && stp >= 1 && stp + 1 < nsteps) {
+                // the copy wave 0 made at the previous step's start, for the next step
+                const u32x4 c = *reinterpret_cast<const u32x4*>(copies + 4 * ((stp - 1) & 3));
+                sh_lo = c[0];
+                sh_hi = c[1];
+            }
             if (issued < nsteps) {
                 wait_lgkm();  // this wave's reads of slot q are done before it is refilled
-                // read before the refill, so the next step's wait for its
-                // block covers it
-                if (share) shared = __hip_atomic_load(share, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 fetch(issued * NW + w, q);
                 ++issued;
             }
@@ -1463,10 +1508,10 @@ __global__ __launch_bounds__(NW * 64) void deepselect_ring_kernel(Params p) {
                                   (uint32_t)p.k,
                                   (uint32_t)p.B2,
                                   ring,
-                                  p.ws_share ? p.ws_share + g.row : nullptr};
+                                  p.ws_share ? p.ws_share + g.row * kCellWords : nullptr};
         sm.run();
         DS_PROF(st, 14);
-        final_select<D, NW>(s, st, (uint32_t)p.k);
+        final_select<D, NW>(s, st, (uint32_t)p.k, p.ws_share != nullptr);
         DS_PROF(st, 11);
         if (p.split == 1)
             write_row<D, NW>(s, p, g.row, st.len, st.W, st.A, st.R, st.maxlen);
@@ -1829,7 +1874,9 @@ __device__ __forceinline__ int32_t merge_bulk(Lds<D>& s, RunState& st, const Par
             c[b] = 0;
             most = cnt[b] > most ? cnt[b] : most;
         }
-        for (uint32_t e0 = 0; e0 < most; e0 += 64 * kBC) {
+        // the first chunk is taken whatever the counts, so its loads need
+        // not wait for them (counts read from the workspace)
+        for (uint32_t e0 = 0; e0 == 0u || e0 < most; e0 += 64 * kBC) {
             PartChunk<kPkParts> pc[kBP];
 #pragma unroll
             for (int b = 0; b < kBP; ++b) pc[b].load_keys(p, row, part[b], e0, cnt[b]);
@@ -1974,7 +2021,9 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
             build_order<NW>(s.perm, p.seed, row, 1, 0, S, s.base);
             DS_PROF(st, 1);
             const int32_t trig = merge_bulk<D, NW, kPkParts>(s, st, p, row, pcnt, [&](int64_t part) -> uint32_t {
-                return counted ? uniform(p.ws_cnt[row * S + part]) : k;
+                if (!counted) return k;
+                return S <= 64 ? uniform(__builtin_amdgcn_readlane(part_cnt, (int)part))
+                               : uniform(p.ws_cnt[row * S + part]);
             });
             DS_PROF(st, 2);
             if (trig < S) compact<D, NW>(s, st, k);
@@ -2061,6 +2110,9 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
         maxlen = st.maxlen > maxlen ? st.maxlen : maxlen;
         DS_PROF(st, 5);
         write_row<D, NW>(s, p, row, st.len, W, A, R, maxlen);
+        // every part of the row has ended (the part kernel came before): its
+        // shared threshold cell is left zero for the next call
+        if (p.ws_share && threadIdx.x == 0) p.ws_share[row * kCellWords] = 0u;
         DS_PROF(st, 6);
 #ifdef DS_PROFILE
         st.prof_flush(2048);
@@ -2068,11 +2120,12 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
     }
 }
 
-// Clear n 64-bit words (the rows' shared threshold cells, before the parts
-// start): a kernel, not a memset, so that the call stays capturable.
+// Clear n shared threshold cells (kCellWords apart; those not known to be
+// zero, before the parts start): a kernel, not a memset, so that the call
+// stays capturable.
 __global__ void deepselect_zero_kernel(uint64_t* p, int64_t n) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
+        p[i * kCellWords] = 0u;
 }
 
 // ===========================================================================
@@ -2175,6 +2228,7 @@ static DevInfo g_dev[kMaxDevices];
 struct WsBuf {
     void* ptr = nullptr;
     size_t bytes = 0;
+    bool zeroed = false;  // its kCells reserved shared-threshold cells have been cleared
 };
 static std::mutex g_ws_mu;
 static std::map<std::tuple<int, void*, std::thread::id>, WsBuf> g_ws;
@@ -2195,7 +2249,7 @@ static int device_info(int dev, DevInfo& out) {
 }
 
 // Caller holds g_ws_mu (until its kernels are queued).
-static int library_workspace(int dev, hipStream_t stream, size_t bytes, void** out) {
+static int library_workspace(int dev, hipStream_t stream, size_t bytes, void** out, bool** zeroed) {
     const std::thread::id tid = stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id();
     WsBuf& w = g_ws[std::make_tuple(dev, (void*)stream, tid)];
     if (w.bytes < bytes) {
@@ -2206,11 +2260,13 @@ static int library_workspace(int dev, hipStream_t stream, size_t bytes, void** o
             w.bytes = 0;
         }
         void* ptr = nullptr;
+        w.zeroed = false;
         if (hipMalloc(&ptr, bytes) != hipSuccess) return DS_ERR_HIP;
         w.ptr = ptr;
         w.bytes = bytes;
     }
     *out = w.ptr;
+    *zeroed = &w.zeroed;
     return DS_OK;
 }
 
@@ -2298,8 +2354,14 @@ static int launch_all(KernelKind kind, int units, int waves, bool vec, Params pr
 // code never passes `scratch` itself to a kernel (on the host it names a
 // stand-in, not device memory): it uses the address hipGetSymbolAddress gives
 // for the current device, taken once per device.
+// The first kCells cells (kCellWords * 8 bytes each) are the reserved
+// shared-threshold cells; calls fit when the workspace they would need from
+// a caller fits in the rest.
 constexpr size_t kScratchBytes = (size_t)8 << 20;
+constexpr size_t kScratchFree = kScratchBytes - (size_t)kCells * kCellWords * 8;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+// per device: the scratch's reserved cells have been cleared
+static std::atomic<bool> g_scratch_zeroed[kMaxDevices];
 
 static int scratch_of(int dev, void** out) {
     if (dev < 0 || dev >= kMaxDevices) return DS_ERR_HIP;
@@ -2330,8 +2392,8 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     if (req_kernel < kAuto || req_kernel > kGeneric) return DS_ERR_BLOCK;
     const int sorted = opt ? opt->sorted : 0;
     if (sorted != 0 && sorted != 1) return DS_ERR_BLOCK;
-    const int share = opt ? opt->share_threshold : 0;
-    if (share != 0 && share != 1) return DS_ERR_BLOCK;
+    const int share_req = opt ? opt->share_threshold : 0;
+    if (share_req != 0 && share_req != 1) return DS_ERR_BLOCK;
     // fused sampling: on sorted output, k within one register sort (4 words a
     // thread of 256)
     const bool sampling = opt && (opt->probs || opt->sample_u);
@@ -2417,21 +2479,52 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     prm.inv_temp = inv_temp;
     prm.top_p = top_p;
     prm.L = L;
+    // Shared thresholds act in the ring kernel only, and from about the
+    // fourth step of a wave on (a published T reaches the other parts' filter
+    // two steps after it goes out): parts with fewer steps run as without it.
+    const bool share = share_req && S > 1 && kind == kRing &&
+                       ceil_div(ceil_div(ceil_div(n, B), S), waves) >= kShareMinSteps;
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     std::unique_lock<std::mutex> ws_lock;  // held while a library workspace is in use
+    // Shared-threshold cells: the merge leaves every cell of its rows zero, so
+    // the kCells cells reserved at the start of a library workspace or of the
+    // scratch (which no other array of any call overlaps) stay zero from one
+    // call to the next once they have been cleared. A call clears what it
+    // cannot know to be zero: all its cells in a caller workspace; the
+    // reserved cells until an eager (not captured) clear has been queued;
+    // cells past the reserved ones.
+    bool* ws_zeroed = nullptr;                    // library workspace (under g_ws_mu)
+    std::atomic<bool>* sc_zeroed = nullptr;       // scratch
+    int64_t clear0 = 0, clear1 = 0;               // cells [clear0, clear1) to clear
+    bool eager_clear = false;                     // the reserved cells are cleared by this call, eagerly
     if (S > 1) {
-        const WsLayout wl = make_ws_layout(batch, k, S);
+        const bool own = noalloc || !(opt && opt->workspace);
+        const WsLayout wl = make_ws_layout(batch, k, S, own ? kCells : 0);
         void* ws = nullptr;
         if (noalloc) {
-            if (wl.total > kScratchBytes) return DS_ERR_SCRATCH;
+            if (make_ws_layout(batch, k, S).total > kScratchFree) return DS_ERR_SCRATCH;
             if ((st = scratch_of(dev, &ws)) != DS_OK) return st;
-        } else if (opt && opt->workspace) {
+            sc_zeroed = &g_scratch_zeroed[dev];
+        } else if (!own) {
             if (opt->workspace_bytes < wl.total) return DS_ERR_WORKSPACE;
             ws = opt->workspace;
         } else {
             ws_lock = std::unique_lock<std::mutex>(g_ws_mu);
-            if ((st = library_workspace(dev, hs, wl.total, &ws)) != DS_OK) return st;
+            if ((st = library_workspace(dev, hs, wl.total, &ws, &ws_zeroed)) != DS_OK) return st;
+        }
+        if (share) {
+            clear1 = batch;
+            if (own) {
+                const bool zeroed = ws_zeroed ? *ws_zeroed : sc_zeroed->load();
+                if (zeroed) {
+                    clear0 = std::min<int64_t>(batch, kCells);
+                } else {
+                    clear1 = std::max<int64_t>(batch, kCells);
+                    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+                    eager_clear = hipStreamIsCapturing(hs, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone;
+                }
+            }
         }
         unsigned char* w = reinterpret_cast<unsigned char*>(ws);
         prm.ws_keys = reinterpret_cast<uint32_t*>(w + wl.keys);
@@ -2442,14 +2535,26 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
         prm.ws_share = share ? reinterpret_cast<uint64_t*>(w + wl.share) : nullptr;
     }
     const int64_t items = batch * S;
-    if (prm.ws_share) {
-        const int64_t blocks = std::min<int64_t>(ceil_div(batch, 256), 1024);
-        hipLaunchKernelGGL(deepselect_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, hs, prm.ws_share, batch);
+    if (clear1 > clear0) {
+        const int64_t blocks = std::min<int64_t>(ceil_div(clear1 - clear0, 256), 1024);
+        hipLaunchKernelGGL(deepselect_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, hs,
+                           prm.ws_share + clear0 * kCellWords, clear1 - clear0);
         if (hipGetLastError() != hipSuccess) return DS_ERR_HIP;
     }
-    if (dtype == DS_F32) return launch_all<F32T, F32T>(kind, units, waves, vec, prm, hs, items);
-    if (packed) return launch_all<BF16P, BF16T>(kind, units, waves, vec, prm, hs, items);
-    return launch_all<BF16T, BF16T>(kind, units, waves, vec, prm, hs, items);
+    int rc;
+    if (dtype == DS_F32)
+        rc = launch_all<F32T, F32T>(kind, units, waves, vec, prm, hs, items);
+    else if (packed)
+        rc = launch_all<BF16P, BF16T>(kind, units, waves, vec, prm, hs, items);
+    else
+        rc = launch_all<BF16T, BF16T>(kind, units, waves, vec, prm, hs, items);
+    if (prm.ws_share) {
+        // a failed launch may leave a part kernel's cells without their merge
+        const bool zeroed = rc == DS_OK && (eager_clear || (ws_zeroed ? *ws_zeroed : sc_zeroed && sc_zeroed->load()));
+        if (ws_zeroed) *ws_zeroed = zeroed;
+        if (sc_zeroed) sc_zeroed->store(zeroed);
+    }
+    return rc;
 }
 
 }  // namespace ds
@@ -2497,7 +2602,7 @@ int deepselect_topk_noalloc(const void* x, int dtype, int64_t batch, int64_t N, 
     }
 }
 
-size_t deepselect_scratch_bytes(void) { return ds::kScratchBytes; }
+size_t deepselect_scratch_bytes(void) { return ds::kScratchFree; }
 
 #ifdef DS_PROFILE
 // Profiling builds only: copy out (and clear) the per-wave cycle counts.

@@ -416,9 +416,10 @@ __device__ __forceinline__ uint32_t pick_bin(const uint32_t* folded, uint32_t& r
 // position, so no group overwrites an entry a later group still reads.
 // Dropped entries are stored to a per-lane junk slot past the buffer, so the
 // stores need no branch.
+// Returns the number of entries kept (the same in every thread).
 template <class D, int NW>
-__device__ __forceinline__ void partition_keep(typename D::Key* keys, uint32_t* idx, uint32_t* tot, uint32_t n,
-                                               uint32_t kth, uint32_t need, uint32_t junk) {
+__device__ __forceinline__ uint32_t partition_keep(typename D::Key* keys, uint32_t* idx, uint32_t* tot, uint32_t n,
+                                                   uint32_t kth, uint32_t need, uint32_t junk) {
     constexpr int NT = NW * 64, R = kRoundsPerGroup;
     const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
     const uint32_t nch = (n + kChunk - 1) / kChunk;
@@ -503,6 +504,8 @@ __device__ __forceinline__ void partition_keep(typename D::Key* keys, uint32_t* 
         }
         par ^= 1u;
     }
+    const uint32_t tied = run >> 16;
+    return (run & 0xFFFFu) + (tied < need ? tied : need);
 }
 
 // The rest of a select once the bin of the k-th key holds few keys: every

@@ -27,6 +27,7 @@ constexpr int64_t kPartBytesMax = (int64_t)1 << 31;  // 32-bit buffer offsets pe
 constexpr int kChunk = 8;                 // candidate entries per thread and select round
 constexpr int kRoundsPerGroup = 2;        // select rounds whose entries a thread holds at once
 constexpr int kGather = 256;              // radix bins this small are finished by every wave alone
+constexpr int kMiscWords = 32;            // [16, 32): four copies of the row's shared cell
 
 DS_HD inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 DS_HD inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -62,7 +63,7 @@ struct Layout {
     uint32_t tot;    // 2 x rounds x waves per-wave totals of the select partition
     uint32_t cnt;    // 2 x waves per-wave counts (block loop)
     uint32_t perm;   // block order (uint16 per block)
-    uint32_t misc;   // 16 uint32 of broadcast scratch
+    uint32_t misc;   // kMiscWords uint32 of broadcast scratch
     uint32_t ring;   // streaming ring: waves x ring_depth blocks of ring_units KiB (0 if none)
     uint32_t sort;   // sorted output: next_pow2(k) uint64 sort words (0 if not asked for)
     uint32_t pcnt;   // merge: one count per part (0 if none)
@@ -107,7 +108,7 @@ inline Layout make_layout_raw(int key_bytes, int64_t cap, int64_t order_n, int w
     L.perm = (uint32_t)off;
     off = align_up(off + (size_t)order_n * 2, 16);
     L.misc = (uint32_t)off;
-    off += 16 * 4;
+    off += kMiscWords * 4;
     L.total = (uint32_t)align_up(off, 16);
     L.cap = (int32_t)cap;
     L.junk = (int32_t)capp;
@@ -173,10 +174,22 @@ struct WsLayout {
     size_t keys, idx, stats, cnt, tkey, share, total;
 };
 
-inline WsLayout make_ws_layout(int64_t batch, int64_t k, int64_t S) {
+// Shared-threshold cells: one uint64 per row, each on a 128-byte line of its
+// own (the rows' parts update and read their cells while other rows do the
+// same). A workspace the library owns, and the static scratch, keep kCells of
+// them reserved at their start, whatever the shape of the call.
+constexpr int64_t kCells = 1024;
+constexpr int64_t kCellWords = 16;  // uint64 words from one row's cell to the next
+
+// The shared-threshold cells come first: max(batch, cells) of them, so with
+// cells = kCells the first kCells sit at the same place for every call and no
+// other array of any call overlaps them.
+inline WsLayout make_ws_layout(int64_t batch, int64_t k, int64_t S, int64_t cells = 0) {
     WsLayout w{};
     if (S <= 1) return w;
     size_t off = 0;
+    w.share = off;  // each row's shared threshold key + 1 (uint64; the merge leaves it 0)
+    off = align_up(off + (size_t)std::max(batch, cells) * kCellWords * 8, 256);
     w.keys = off;
     off = align_up(off + (size_t)batch * S * k * 4, 256);
     w.idx = off;
@@ -187,8 +200,6 @@ inline WsLayout make_ws_layout(int64_t batch, int64_t k, int64_t S) {
     off = align_up(off + (size_t)batch * S * 4, 256);
     w.tkey = off;  // each part's k-th key when it has k results, else 0 (uint32)
     off = align_up(off + (size_t)batch * S * 4, 256);
-    w.share = off;  // each row's shared threshold key + 1 (uint64, zero between calls)
-    off = align_up(off + (size_t)batch * 8, 256);
     w.total = off;
     return w;
 }
