@@ -131,7 +131,9 @@ struct Lds {
     uint32_t* gathered;
     uint32_t* cnt;
     uint16_t* perm;
-    uint32_t* misc;  // [2] gathered-key counter, [8 + w] wave w's largest appended key,
+    uint32_t* misc;  // [2] gathered-key counter, [8 + w] wave w's largest appended key
+                     // (when sorting the results: [8 + w] and [16 + w] wave w's smallest
+                     // and largest result key),
                      // [16, 32) four copies of the row's shared threshold cell
                      // (16 bytes each, the cell in the first 8)
     unsigned char* base;
@@ -1024,15 +1026,26 @@ __device__ __forceinline__ void bitonic_lds(uint64_t* a, uint32_t n2) {
 
 // A stage of distance J < E inside each thread's E words (i0 = E * thread,
 // so word i0 + e has bit `size` set when i0 or e has).
-template <int E, int J>
-__device__ __forceinline__ void bitonic_in_thread(uint64_t (&v)[E], uint32_t i0, uint32_t size) {
+// The word of x and o that a side keeping the larger (big) or the smaller
+// one ends with: a 32-bit word through min and max, a 64-bit one through one
+// compare.
+__device__ __forceinline__ uint32_t keep_side(uint32_t x, uint32_t o, bool big) {
+    const uint32_t mx = o > x ? o : x, mn = o > x ? x : o;
+    return big ? mx : mn;
+}
+__device__ __forceinline__ uint64_t keep_side(uint64_t x, uint64_t o, bool big) {
+    return (o > x) == big ? o : x;
+}
+
+template <int E, int J, class W>
+__device__ __forceinline__ void bitonic_in_thread(W (&v)[E], uint32_t i0, uint32_t size) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         if ((e & J) == 0) {
-            const uint64_t x = v[e], y = v[e | J];
-            const bool swap = ((i0 | (uint32_t)e) & size) == 0 ? x < y : x > y;
-            v[e] = swap ? y : x;
-            v[e | J] = swap ? x : y;
+            const W x = v[e], y = v[e | J];
+            const bool desc = ((i0 | (uint32_t)e) & size) == 0;
+            v[e] = keep_side(x, y, desc);
+            v[e | J] = keep_side(y, x, !desc);
         }
     }
 }
@@ -1064,16 +1077,24 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
 }
 
 // A stage of distance j = D * E: word e of this lane meets word e of lane
-// (lane ^ D); all E words of a thread keep the same side.
-template <int E, int D>
-__device__ __forceinline__ void bitonic_lane_stage(uint64_t (&v)[E], uint32_t i0, uint32_t size) {
+// (lane ^ D); all E words of a thread keep the same side. A 64-bit word
+// moves as two 32-bit halves.
+template <int D>
+__device__ __forceinline__ uint32_t lane_xor_w(uint32_t v) {
+    return lane_xor<D>(v);
+}
+template <int D>
+__device__ __forceinline__ uint64_t lane_xor_w(uint64_t v) {
+    const uint32_t lo = lane_xor<D>((uint32_t)v);
+    const uint32_t hi = lane_xor<D>((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+template <int E, int D, class W>
+__device__ __forceinline__ void bitonic_lane_stage(W (&v)[E], uint32_t i0, uint32_t size) {
     const bool big = keeps_larger(i0, (uint32_t)(D * E), size);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const uint32_t lo = lane_xor<D>((uint32_t)v[e]);
-        const uint32_t hi = lane_xor<D>((uint32_t)(v[e] >> 32));
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        v[e] = (o > v[e]) == big ? o : v[e];
+        v[e] = keep_side(v[e], lane_xor_w<D>(v[e]), big);
     }
 }
 
@@ -1083,8 +1104,8 @@ __device__ __forceinline__ void bitonic_lane_stage(uint64_t (&v)[E], uint32_t i0
 // barriers) while j >= 64*E, then across the lanes of the wave with vector
 // lane moves while j >= E, then inside the thread. Waves without a word only
 // take part in the barriers.
-template <int NW, int E>
-__device__ __forceinline__ void bitonic_regs(uint64_t (&v)[E], uint32_t n2, uint64_t* buf) {
+template <int NW, int E, class W>
+__device__ __forceinline__ void bitonic_regs(W (&v)[E], uint32_t n2, W* buf, RunState* prof = nullptr) {
     static_assert(E == 4, "in-thread stages of distance 1 and 2");
     const uint32_t i0 = threadIdx.x * E;
     const bool holds = i0 < n2;
@@ -1101,13 +1122,16 @@ __device__ __forceinline__ void bitonic_regs(uint64_t (&v)[E], uint32_t n2, uint
             lds_barrier();
             if (holds) {
                 const bool big = keeps_larger(i0, j, size);  // the same for the thread's E words
+                W o[E];  // all reads issued before the first compare
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const uint64_t o = buf[(i0 + e) ^ j];
-                    v[e] = (o > v[e]) == big ? o : v[e];
-                }
+                for (int e = 0; e < E; ++e) o[e] = buf[(i0 + e) ^ j];
+#pragma unroll
+                for (int e = 0; e < E; ++e) v[e] = keep_side(v[e], o[e], big);
             }
         }
+#ifdef DS_PROFILE
+        if (prof) prof->prof_mark(11);  // stages through LDS
+#endif
         if (!wave_holds) continue;
         if (j == 32u * E) bitonic_lane_stage<E, 32>(v, i0, size), j >>= 1;
         if (j == 16u * E) bitonic_lane_stage<E, 16>(v, i0, size), j >>= 1;
@@ -1115,8 +1139,14 @@ __device__ __forceinline__ void bitonic_regs(uint64_t (&v)[E], uint32_t n2, uint
         if (j == 4u * E) bitonic_lane_stage<E, 4>(v, i0, size), j >>= 1;
         if (j == 2u * E) bitonic_lane_stage<E, 2>(v, i0, size), j >>= 1;
         if (j == 1u * E) bitonic_lane_stage<E, 1>(v, i0, size), j >>= 1;
+#ifdef DS_PROFILE
+        if (prof) prof->prof_mark(12);  // stages across lanes
+#endif
         if (j == 2u) bitonic_in_thread<E, 2>(v, i0, size), j >>= 1;
         if (j == 1u) bitonic_in_thread<E, 1>(v, i0, size);
+#ifdef DS_PROFILE
+        if (prof) prof->prof_mark(13);  // stages inside the thread
+#endif
     }
 }
 
@@ -1280,15 +1310,137 @@ __device__ __forceinline__ void write_sorted(Lds<D>& s, const Params& p, int64_t
     const uint32_t k = (uint32_t)p.k;
     const uint32_t n2 = k <= 1u ? 1u : 1u << (32 - __clz(k - 1u));
     if (n2 <= (uint32_t)(E * NW * 64)) {
+#ifdef DS_PROFILE
+        RunState pst;  // cycle accounting of the sort's phases only
+#endif
         const uint32_t i0 = threadIdx.x * E;
         uint64_t v[E];
+        uint32_t lo = 0xFFFFFFFFu, hi = 0;  // the results' smallest and largest keys
 #pragma unroll
-        for (int e = 0; e < E; ++e) v[e] = i0 + e < cnt ? sort_word<D>(s, i0 + e) : 0ull;
-        bitonic_regs<NW, E>(v, n2, buf);
+        for (int e = 0; e < E; ++e) {
+            v[e] = i0 + e < cnt ? sort_word<D>(s, i0 + e) : 0ull;
+            if (i0 + e < cnt) {
+                const uint32_t key = (uint32_t)(v[e] >> 32);
+                lo = key < lo ? key : lo;
+                hi = key > hi ? key : hi;
+            }
+        }
+        // When the keys span few enough values, key - lo and the column fit
+        // one 32-bit word, (key - lo) << cb | (cmask - column) with cb the
+        // bit length of N (so the second field is at least 1 and every
+        // result stays above the padding 0): the same order, at half the
+        // lane moves and with 32-bit compares.
+        const uint32_t wlo = wave_min(lo), whi = wave_max(hi);
+        if (lane_id() == 0) {
+            s.misc[8 + wave_id()] = wlo;   // the final select no longer reads these
+            s.misc[16 + wave_id()] = whi;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const uint32_t a = s.misc[8 + w], b = s.misc[16 + w];
+            lo = a < lo ? a : lo;
+            hi = b > hi ? b : hi;
+        }
+        lo = uniform(lo);
+        hi = uniform(hi);
+        DS_PROF(pst, 7);
+        const uint32_t cb = 32u - (uint32_t)__clz((uint32_t)p.n);
+        const uint32_t cmask = (1u << cb) - 1u;
+        const bool narrow = cnt > 0u && cb < 32u && (uint64_t)(hi - lo) < ((uint64_t)1 << (32u - cb));
+        // 16-bit keys spanning more: the key's dense rank (the number of
+        // distinct result keys above it, below n2) takes its place,
+        // (R - rank) << cb | (cmask - column) with R = 2^rb - 1, and a table
+        // in the candidate key array gives the key of each rank back. The
+        // ranks come from a bitmap of the keys present (bit key - lo) and a
+        // prefix count of its bits from the top, both in the sort buffer.
+        const uint32_t rb = n2 > 1u ? 32u - (uint32_t)__clz(n2 - 1u) : 1u;
+        const uint32_t nbw = ((hi - lo) >> 5) + 1u;  // bitmap words
+        const bool ranked = D::kBits == 16 && !narrow && cnt > 0u && rb + cb <= 32u && nbw <= n2;
+        if (narrow || ranked) {
+            uint32_t v32[E];
+            const uint32_t R = (1u << rb) - 1u;
+            uint16_t* keyof = reinterpret_cast<uint16_t*>(s.keys);  // rank -> key (read above, in v)
+            if (narrow) {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    v32[e] = i0 + e < cnt ? (((uint32_t)(v[e] >> 32) - lo) << cb) | (cmask - ~(uint32_t)v[e]) : 0u;
+            } else {
+                constexpr uint32_t NT = NW * 64;
+                uint32_t* bm = reinterpret_cast<uint32_t*>(buf);
+                uint32_t* above = bm + nbw;  // set bits in the words past each word
+                for (uint32_t j = threadIdx.x; j < nbw; j += NT) bm[j] = 0u;
+                lds_barrier();
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    if (i0 + e < cnt) {
+                        const uint32_t d = (uint32_t)(v[e] >> 32) - lo;
+                        atomicOr(&bm[d >> 5], 1u << (d & 31u));
+                    }
+                }
+                lds_barrier();
+                // thread t counts words [t*per, t*per + per); the bits past
+                // its words are the total less an inclusive prefix over the
+                // threads
+                const uint32_t per = (nbw + NT - 1u) / NT;
+                const uint32_t w0 = threadIdx.x * per;
+                uint32_t mine = 0;
+                for (uint32_t j = w0; j < w0 + per && j < nbw; ++j) mine += (uint32_t)__builtin_popcount(bm[j]);
+                const uint32_t incl = wave_prefix_sum(mine);
+                if (lane_id() == 63) s.tot[wave_id()] = incl;
+                lds_barrier();
+                uint32_t before = 0, total = 0;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    const uint32_t t = s.tot[w];
+                    before += w < wave_id() ? t : 0u;
+                    total += t;
+                }
+                uint32_t run = total - (before + incl);  // bits in the words past this thread's
+                for (uint32_t j = (w0 + per < nbw ? w0 + per : nbw); j > w0; --j) {
+                    above[j - 1u] = run;
+                    run += (uint32_t)__builtin_popcount(bm[j - 1u]);
+                }
+                lds_barrier();
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    if (i0 + e < cnt) {
+                        const uint32_t key = (uint32_t)(v[e] >> 32), d = key - lo;
+                        const uint32_t rank =
+                            above[d >> 5] + (uint32_t)__builtin_popcount((bm[d >> 5] >> (d & 31u)) >> 1);
+                        keyof[rank] = (uint16_t)key;
+                        v32[e] = ((R - rank) << cb) | (cmask - ~(uint32_t)v[e]);
+                    } else {
+                        v32[e] = 0u;
+                    }
+                }
+            }
+            DS_PROF(pst, 8);
+#ifdef DS_PROFILE
+            bitonic_regs<NW, E>(v32, n2, reinterpret_cast<uint32_t*>(buf), &pst);
+#else
+            bitonic_regs<NW, E>(v32, n2, reinterpret_cast<uint32_t*>(buf));
+#endif
+            if (ranked) lds_barrier();  // the rank table is complete
+            DS_PROF(pst, 9);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const uint32_t key = narrow ? (v32[e] >> cb) + lo : (uint32_t)keyof[R - (v32[e] >> cb)];
+                v[e] = v32[e] != 0u ? ((uint64_t)key << 32) | (uint32_t)~(cmask - (v32[e] & cmask)) : 0ull;
+            }
+        } else {
+            DS_PROF(pst, 8);
+            bitonic_regs<NW, E>(v, n2, buf);
+            DS_PROF(pst, 9);
+        }
         if (p.probs || p.sample_u) softmax_sample<D, NW, E>(v, i0, cnt, p, row, s.tot);
 #pragma unroll
         for (int e = 0; e < E; ++e)
             if (i0 + e < k) put_sorted<D>(p, row, i0 + e, v[e], cnt);
+        DS_PROF(pst, 10);
+#ifdef DS_PROFILE
+        if (p.split > 1) pst.prof_flush(2048);
+#endif
     } else {
         for (uint32_t j = threadIdx.x; j < n2; j += NW * 64) buf[j] = j < cnt ? sort_word<D>(s, j) : 0ull;
         bitonic_lds<NW>(buf, n2);

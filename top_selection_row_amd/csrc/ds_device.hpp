@@ -219,6 +219,9 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
     return uniform(__builtin_amdgcn_readlane(v, 63));
 }
 
+// Smallest value over the wave, returned uniform (the largest complement).
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) { return ~wave_max(~v); }
+
 // Inclusive prefix sum over the 64 lanes (lane l gets the sum over lanes <= l)
 // with DPP moves only: shifts by 1, 2, 4 and 8 inside each row of 16 lanes,
 // then the last lane of row 0 (2) is added to row 1 (3) and the last lane of
