@@ -189,8 +189,14 @@ __device__ __forceinline__ void select_buffer(Lds<D>& s, RunState& st, uint32_t 
         hi = v > hi ? v : hi;
     }
     hi = uniform(hi);
+    // the barrier above made the appends visible: the select starts without one
+#ifdef DS_PROFILE
     st.tkey = select_topk<D, NW>(s.keys, s.idx, s.hist, s.fold, s.tot, s.gathered, s.misc + 2, s.junk, st.len, k, lo,
-                                  hi > lo ? hi : lo);
+                                  hi > lo ? hi : lo, true, true, [&](int c) { st.prof_mark(c); });
+#else
+    st.tkey = select_topk<D, NW>(s.keys, s.idx, s.hist, s.fold, s.tot, s.gathered, s.misc + 2, s.junk, st.len, k, lo,
+                                  hi > lo ? hi : lo, true, true);
+#endif
     st.tset = true;
     st.fkey = st.fset && st.fkey > st.tkey ? st.fkey : st.tkey;
     st.fset = true;
@@ -602,8 +608,40 @@ struct RingStreamer {
     // count, in the low bits, with bit 31 set), one 32-bit compare per element
     // (the threshold's sign fixed at compile time).
     static constexpr bool kMasks = U * V <= 32;
+    // bfloat16 masks hold the low halves of the lane's words in bits 0-15 and
+    // the high halves in bits 16-31 (element q of unit u: word u*4 + q/2,
+    // half q%2), so one packed 16-bit test gives a word's two bits at once;
+    // float32 masks (and 64-bit ones) hold element q of unit u at u*V + q.
+    static constexpr bool kPkMask = D::kBytes == 2 && kMasks;
+    static __device__ __forceinline__ constexpr int mask_bit(int u, int q) {
+        return kPkMask ? ((q & 1) * 16 + u * 4 + (q >> 1)) : (u * V + q);
+    }
     template <bool kNeg>
     __device__ __forceinline__ uint32_t lane_mask(const BlockRegs<U>& r, uint32_t thr) const {
+        if constexpr (kPkMask) {
+            // Both halves of a word against the threshold's 16 bits with one
+            // saturating packed subtract whose sign bits are the tests: above
+            // a threshold at or over +0, t - h < 0 (signed halves); below a
+            // negative one's bits, (h ^ 0x8000) - (t ^ 0x8000) < 0 (unsigned
+            // order as signed). The same tests as above_k on the two words.
+            typedef short s2 __attribute__((ext_vector_type(2)));
+            const uint32_t t16 = thr >> 16;
+            const s2 tv = kNeg ? s2{(short)(t16 ^ 0x8000u), (short)(t16 ^ 0x8000u)} : s2{(short)t16, (short)t16};
+            uint32_t m = 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int wi = u * 4 + w;
+                    const uint32_t d = r.v[u][w];
+                    const s2 sv = kNeg ? __builtin_elementwise_sub_sat(__builtin_bit_cast(s2, d ^ 0x80008000u), tv)
+                                       : __builtin_elementwise_sub_sat(tv, __builtin_bit_cast(s2, d));
+                    const uint32_t sb = __builtin_bit_cast(uint32_t, sv);
+                    m |= (sb >> (15 - wi)) & ((1u << wi) | (1u << (16 + wi)));
+                }
+            }
+            return m;
+        }
         uint32_t m = 0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -710,7 +748,7 @@ struct RingStreamer {
 #pragma unroll
                 for (int h = 0; h < V / 4; ++h) {
                     const int q = w * (V / 4) + h;
-                    const int b = u * V + q;
+                    const int b = sizeof(MaskT) == 4 ? mask_bit(u, q) : u * V + q;
                     const bool pred = (m >> b) & 1;
                     uint32_t before;
                     if constexpr (sizeof(MaskT) == 8)
@@ -744,7 +782,14 @@ struct RingStreamer {
         while (m != 0u) {
             const uint32_t e = (uint32_t)__builtin_ctz(m);
             m &= m - 1u;
-            const uint32_t u = e / V, q = e % V;
+            uint32_t u, q;  // the element of bit e (mask_bit's inverse)
+            if constexpr (kPkMask) {
+                u = (e & 15u) >> 2;
+                q = ((e & 3u) << 1) | (e >> 4);
+            } else {
+                u = e / V;
+                q = e % V;
+            }
             const unsigned char* p = lp + u * (64 * 16) + q * D::kBytes;
             const uint32_t raw = D::kBytes == 4 ? *reinterpret_cast<const uint32_t*>(p)
                                                 : (uint32_t)*reinterpret_cast<const uint16_t*>(p);

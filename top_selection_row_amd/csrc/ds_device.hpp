@@ -578,13 +578,22 @@ __device__ __forceinline__ uint32_t finish_gathered(const typename D::Key* keys,
 // RadixSelectTopK: keep the k largest of keys/idx[0, n) (k <= n) in [0, k)
 // and return the k-th largest key. Every key lies in [lo, hi]. Entries
 // [junk, junk+64) of both arrays are scratch for dropped entries. Starts with a
-// barrier (the caller's appends become visible); the histogram copies must be
-// clear on entry and are clear on return.
-template <class D, int NW>
+// barrier (the caller's appends become visible) unless the caller has just
+// passed one (synced); the histogram copies must be clear on entry and are
+// clear on return.
+// `mark(c)` is called after each phase (c: 5 entry, 6 histogram, 7 fold,
+// 8 pick, 9 partition, 10 gathered finish): a cycle-accounting hook of the
+// profiling build, nothing otherwise.
+struct NoMark {
+    __device__ void operator()(int) const {}
+};
+template <class D, int NW, class Mark = NoMark>
 __device__ uint32_t select_topk(typename D::Key* keys, uint32_t* idx, uint32_t* hist, uint32_t* folded,
                                 uint32_t* tot, uint32_t* gathered, uint32_t* gcount, uint32_t junk, uint32_t n,
-                                uint32_t k, uint32_t lo, uint32_t hi, bool all_in = true) {
-    lds_barrier();
+                                uint32_t k, uint32_t lo, uint32_t hi, bool all_in = true, bool synced = false,
+                                Mark mark = {}) {
+    if (!synced) lds_barrier();  // synced: the caller's own barrier made the buffer visible
+    mark(5);
     uint32_t base = lo, span = hi - lo, rank = k;
     int s = span ? 32 - __clz(span) : 0;  // bit length of the span
     s = s > 8 ? s - 8 : 0;
@@ -597,10 +606,13 @@ __device__ uint32_t select_topk(typename D::Key* keys, uint32_t* idx, uint32_t* 
         first = false;
         if (threadIdx.x == 0) *gcount = 0u;
         lds_barrier();
+        mark(6);
         fold_pass<NW>(hist, folded);
         lds_barrier();
+        mark(7);
         uint32_t cnt;
         base += pick_bin(folded, rank, cnt) << s;
+        mark(8);
         if (s == 0) break;
         span = (1u << s) - 1u;
         // gathering pays off when two or more digits remain (32-bit keys);
@@ -608,12 +620,14 @@ __device__ uint32_t select_topk(typename D::Key* keys, uint32_t* idx, uint32_t* 
         if constexpr (D::kBits > 16) {
             if (cnt <= (uint32_t)kGather && s > 8) {
                 base = finish_gathered<D, NW>(keys, n, base, span, s, rank, hist, gathered, gcount);
+                mark(10);
                 break;
             }
         }
         s = s > 8 ? s - 8 : 0;
     }
     partition_keep<D, NW>(keys, idx, tot, n, base, rank, junk);
+    mark(9);
     return base;
 }
 
