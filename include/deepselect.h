@@ -97,8 +97,9 @@ typedef struct ds_options {
     uint64_t *stats;
     /* Device workspace for split rows, or NULL for the library-owned one.
      * Size from deepselect_workspace_bytes; no initial contents are needed. It
-     * holds every part's results (up to k), their count, the part's k-th key
-     * and statistics between the part kernel and the merge kernel, and the
+     * holds every part's results (up to k), their count, the part's k-th and
+     * largest keys and statistics between the part kernel and the merge
+     * kernel, and the
      * rows' shared-threshold cells, so it must not be shared by calls that may
      * overlap. */
     void *workspace;
@@ -196,8 +197,8 @@ int deepselect_topk_ex(const void *x, int dtype, int64_t batch, int64_t N, int64
 /* deepselect_topk_ex for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc. It calls no hipMalloc, hipFree or other allocating routine. The
- * workspace of split rows (every part's results, counts, k-th keys,
- * statistics and shared-threshold cells) lives in a static device array of
+ * workspace of split rows (every part's results, counts, k-th and largest
+ * keys, statistics and shared-threshold cells) lives in a static device array of
  * 8 MiB, one copy per GPU the library runs on, kept until the process ends;
  * its device address is looked up once per device on the first call there.
  * Its first 128 KiB hold 1024 reserved shared-threshold cells (see

@@ -79,6 +79,7 @@ struct Params {
     uint64_t* ws_share;      // per row: the largest part threshold key + 1 (0: none), or NULL
     uint32_t* ws_cnt;        // per part: its number of results
     uint32_t* ws_tkey;       // per part: its k-th key when it has k results, else 0
+    uint32_t* ws_tmax;       // per part: its largest result key (0 without results)
     Layout L;
 };
 
@@ -1564,10 +1565,18 @@ template <class D, int NW>
 __device__ __forceinline__ void write_part(Lds<D>& s, const RunState& st, const Params& p, int64_t slot,
                                            uint32_t part_elem0) {
     // the part's number of results: k, or fewer for a short part or one
-    // filtered by a shared threshold
+    // filtered by a shared threshold; its largest result key is the largest
+    // key appended (that one is always kept), reduced over the waves
+    const uint32_t wmax = wave_max(st.kmax);
+    if (lane_id() == 0) s.misc[8 + wave_id()] = wmax;
+    lds_barrier();
     if (p.ws_cnt && threadIdx.x == 0) {
+        uint32_t tmax = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) tmax = s.misc[8 + w] > tmax ? s.misc[8 + w] : tmax;
         p.ws_cnt[slot] = st.len;
         p.ws_tkey[slot] = st.len == (uint32_t)p.k && st.tset ? st.tkey : 0u;
+        p.ws_tmax[slot] = st.len != 0u ? tmax : 0u;
     }
     if constexpr (is_packed<D>::value) {
         // packed bfloat16 results stay one word each, key << 16 | column
@@ -2071,9 +2080,7 @@ __device__ __forceinline__ int32_t merge_bulk(Lds<D>& s, RunState& st, const Par
             c[b] = 0;
             most = cnt[b] > most ? cnt[b] : most;
         }
-        // the first chunk is taken whatever the counts, so its loads need
-        // not wait for them (counts read from the workspace)
-        for (uint32_t e0 = 0; e0 == 0u || e0 < most; e0 += 64 * kBC) {
+        for (uint32_t e0 = 0; e0 < most; e0 += 64 * kBC) {
             PartChunk<kPkParts> pc[kBP];
 #pragma unroll
             for (int b = 0; b < kBP; ++b) pc[b].load_keys(p, row, part[b], e0, cnt[b]);
@@ -2181,8 +2188,12 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
         // part q's, loaded with the first tiles (more than 64 parts: read
         // where needed)
         const bool counted = p.lengths || p.ws_share;
-        uint32_t part_cnt = k;
+        uint32_t part_cnt = k, part_max = 0xFFFFFFFFu;
         if (counted && S <= 64 && lane_id() < S) part_cnt = p.ws_cnt[row * S + lane_id()];
+        // and their largest keys: a part whose largest key is below the
+        // admission bound (t0 below) admits nothing, so its results are not
+        // read in the bulk phase
+        if (!both && S <= 64 && lane_id() < S) part_max = p.ws_tmax[row * S + lane_id()];
         // the largest k-th key of the parts that hold k results: the k-th of
         // any k elements of the row is at most the row's, so the merge admits
         // only results at or above it (T starts just below it)
@@ -2213,29 +2224,52 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
             cur = swap ? pre1 : pre0;
             nxt = swap ? pre0 : pre1;
         }
-        int64_t j0 = 0;  // the first tile the part-by-part loop takes
-        if (!both) {
+        int64_t j0 = 0;          // the first tile the part-by-part loop takes
+        int64_t tiles_end = tiles;  // and the end
+        // At most one part that can admit results (a part admits none when
+        // its largest key is below t0, or it has none): the order of the
+        // parts changes neither the buffer nor the statistics, so no order
+        // is built and the loop takes that part's tiles alone.
+        bool single = false;
+        int64_t sid = 0;
+        if (!both && S <= 64) {
+            const uint32_t my_cnt = counted ? part_cnt : k;
+            const uint64_t live = __ballot(lane_id() < S && my_cnt != 0u && (t0 == 0u || part_max >= t0));
+            single = __popcll(live) <= 1;
+            sid = live != 0ull ? (int64_t)__builtin_ctzll(live) : -1;
+        }
+        if (single) {
+            tiles_end = sid >= 0 ? (int64_t)tpp : 0;
+            if (tiles_end > 0) load_part_tile<NW, kPkParts>(cur, p, row, sid, 0);
+        } else if (!both) {
             build_order<NW>(s.perm, p.seed, row, 1, 0, S, s.base);
             DS_PROF(st, 1);
-            const int32_t trig = merge_bulk<D, NW, kPkParts>(s, st, p, row, pcnt, [&](int64_t part) -> uint32_t {
+            // results of a part that can admit any (t0 != 0: T = t0 - 1 is set)
+            const auto cnt_of = [&](int64_t part) -> uint32_t {
+                if (S <= 64 && t0 != 0u && uniform(__builtin_amdgcn_readlane(part_max, (int)part)) < t0) return 0u;
                 if (!counted) return k;
                 return S <= 64 ? uniform(__builtin_amdgcn_readlane(part_cnt, (int)part))
                                : uniform(p.ws_cnt[row * S + part]);
-            });
+            };
+            const int32_t trig = merge_bulk<D, NW, kPkParts>(s, st, p, row, pcnt, cnt_of);
             DS_PROF(st, 2);
             if (trig < S) compact<D, NW>(s, st, k);
             j0 = (int64_t)(trig + 1) * tpp;
             if (j0 < tiles) load_merge_tile<NW, kPkParts>(cur, p, s.perm, row, j0, tpp);
         }
-        for (int64_t j = j0; j < tiles; ++j) {
-            if (!both && j + 1 < tiles) load_merge_tile<NW, kPkParts>(nxt, p, s.perm, row, j + 1, tpp);
+        for (int64_t j = j0; j < tiles_end; ++j) {
+            if (single) {
+                if (j + 1 < tiles_end) load_part_tile<NW, kPkParts>(nxt, p, row, sid, (uint32_t)(j + 1));
+            } else if (!both && j + 1 < tiles) {
+                load_merge_tile<NW, kPkParts>(nxt, p, s.perm, row, j + 1, tpp);
+            }
             const uint32_t t0 = (uint32_t)(j % tpp) * TE;
             // results of the part: k, or fewer for a part shorter than k or
             // one filtered by a shared threshold
             uint32_t cnt = k;
             if (counted) {
                 const int64_t i = j / tpp;
-                const int64_t part = both ? (swap ? 1 - i : i) : (int64_t)uniform(s.perm[i]);
+                const int64_t part = single ? sid : both ? (swap ? 1 - i : i) : (int64_t)uniform(s.perm[i]);
                 cnt = S <= 64 ? uniform(__builtin_amdgcn_readlane(part_cnt, (int)part))
                               : uniform(p.ws_cnt[row * S + part]);
             }
@@ -2729,6 +2763,7 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
         prm.ws_stats = reinterpret_cast<uint64_t*>(w + wl.stats);
         prm.ws_cnt = reinterpret_cast<uint32_t*>(w + wl.cnt);
         prm.ws_tkey = reinterpret_cast<uint32_t*>(w + wl.tkey);
+        prm.ws_tmax = reinterpret_cast<uint32_t*>(w + wl.tmax);
         prm.ws_share = share ? reinterpret_cast<uint64_t*>(w + wl.share) : nullptr;
     }
     const int64_t items = batch * S;

@@ -171,7 +171,7 @@ inline Layout make_merge_layout(int dtype, int64_t k, int64_t B2, int64_t S, int
 // Workspace of split rows (device memory): every part's k (key, column) pairs
 // and its four statistics. The merge kernel reads it after the part kernel.
 struct WsLayout {
-    size_t keys, idx, stats, cnt, tkey, share, total;
+    size_t keys, idx, stats, cnt, tkey, tmax, share, total;
 };
 
 // Shared-threshold cells: one uint64 per row, each on a 128-byte line of its
@@ -199,6 +199,8 @@ inline WsLayout make_ws_layout(int64_t batch, int64_t k, int64_t S, int64_t cell
     w.cnt = off;  // each part's number of results (uint32)
     off = align_up(off + (size_t)batch * S * 4, 256);
     w.tkey = off;  // each part's k-th key when it has k results, else 0 (uint32)
+    off = align_up(off + (size_t)batch * S * 4, 256);
+    w.tmax = off;  // each part's largest result key, 0 without results (uint32)
     off = align_up(off + (size_t)batch * S * 4, 256);
     w.total = off;
     return w;
