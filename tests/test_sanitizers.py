@@ -4,7 +4,10 @@
   strings, rejected calls) built host-only with the sanitizers on the host
   pass, linked into tests/host_check.cpp;
 * the C oracle with tests/oracle_check.c, built by gcc with the same
-  sanitizers and OpenMP.
+  sanitizers and OpenMP;
+* the workspace cache (csrc/ds_workspace.hpp) driven from 8 threads with
+  fake streams by tests/ws_check.cpp, once under AddressSanitizer and
+  UndefinedBehaviorSanitizer and once under ThreadSanitizer.
 Each program exits non-zero on a failed expectation; a sanitizer finding
 aborts it. The GPU code is not part of these builds."""
 import os
@@ -57,3 +60,17 @@ def test_oracle_under_sanitizers(tmp_path):
           os.path.join(ROOT, "tests", "oracle_check.c"), "-o", exe])
     res = _run([exe], env=SAN_ENV)
     assert "0 failures" in res.stdout
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not found")
+@pytest.mark.parametrize("san", [["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"],
+                                 ["-fsanitize=thread"]], ids=["asan-ubsan", "tsan"])
+def test_workspace_cache_under_threads(tmp_path, san):
+    # every call frees a buffer only after synchronising its stream, while
+    # holding the lock from the choice of the workspace until its use is queued
+    exe = str(tmp_path / "ws_check")
+    _run(["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", *san, "-pthread",
+          os.path.join(ROOT, "tests", "ws_check.cpp"), "-o", exe])
+    env = dict(SAN_ENV, TSAN_OPTIONS="halt_on_error=1")
+    res = _run([exe], env=env)
+    assert "no free of a queued buffer" in res.stdout

@@ -51,6 +51,7 @@
 #include "../../include/deepselect.h"
 #include "ds_device.hpp"
 #include "ds_plan.hpp"
+#include "ds_workspace.hpp"
 
 namespace ds {
 
@@ -2451,18 +2452,18 @@ constexpr int kMaxDevices = 64;
 static std::mutex g_mu;
 static DevInfo g_dev[kMaxDevices];
 
-// Library-owned split workspaces, one per (device, stream) -- and per thread
-// for hipStreamPerThread, whose one handle names a different stream in every
-// thread. g_ws_mu is held from the choice of a workspace until the call's
-// kernels are queued, so a concurrent call that grows (frees) the same
-// workspace waits for them to be queued and then synchronises the stream.
-struct WsBuf {
-    void* ptr = nullptr;
-    size_t bytes = 0;
-    bool zeroed = false;  // its kCells reserved shared-threshold cells have been cleared
+// Library-owned split workspaces (ds_workspace.hpp): one per (device,
+// stream), and per thread for hipStreamPerThread, whose one handle names a
+// different stream in every thread. The cache's lock is held from the choice
+// of a workspace until the call's kernels are queued.
+struct HipWsOps {
+    bool per_thread(void* stream) const { return reinterpret_cast<hipStream_t>(stream) == hipStreamPerThread; }
+    int sync(void* stream) const { return hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)) != hipSuccess; }
+    int release(void* ptr) const { return hipFree(ptr) != hipSuccess; }
+    int allocate(void** ptr, size_t bytes) const { return hipMalloc(ptr, bytes) != hipSuccess; }
 };
-static std::mutex g_ws_mu;
-static std::map<std::tuple<int, void*, std::thread::id>, WsBuf> g_ws;
+static HipWsOps g_ws_ops;
+static WsCache<HipWsOps> g_ws;
 
 static int device_info(int dev, DevInfo& out) {
     if (dev < 0 || dev >= kMaxDevices) return DS_ERR_HIP;
@@ -2479,25 +2480,12 @@ static int device_info(int dev, DevInfo& out) {
     return DS_OK;
 }
 
-// Caller holds g_ws_mu (until its kernels are queued).
+// Caller holds g_ws.mu() (until its kernels are queued).
 static int library_workspace(int dev, hipStream_t stream, size_t bytes, void** out, bool** zeroed) {
-    const std::thread::id tid = stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id();
-    WsBuf& w = g_ws[std::make_tuple(dev, (void*)stream, tid)];
-    if (w.bytes < bytes) {
-        if (w.ptr) {
-            if (hipStreamSynchronize(stream) != hipSuccess) return DS_ERR_HIP;
-            if (hipFree(w.ptr) != hipSuccess) return DS_ERR_HIP;
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
-        void* ptr = nullptr;
-        w.zeroed = false;
-        if (hipMalloc(&ptr, bytes) != hipSuccess) return DS_ERR_HIP;
-        w.ptr = ptr;
-        w.bytes = bytes;
-    }
-    *out = w.ptr;
-    *zeroed = &w.zeroed;
+    WsBuf* w = nullptr;
+    if (g_ws.acquire(g_ws_ops, dev, reinterpret_cast<void*>(stream), bytes, &w) != 0) return DS_ERR_HIP;
+    *out = w->ptr;
+    *zeroed = &w->zeroed;
     return DS_OK;
 }
 
@@ -2725,7 +2713,7 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     // cannot know to be zero: all its cells in a caller workspace; the
     // reserved cells until an eager (not captured) clear has been queued;
     // cells past the reserved ones.
-    bool* ws_zeroed = nullptr;                    // library workspace (under g_ws_mu)
+    bool* ws_zeroed = nullptr;                    // library workspace (under g_ws.mu())
     std::atomic<bool>* sc_zeroed = nullptr;       // scratch
     int64_t clear0 = 0, clear1 = 0;               // cells [clear0, clear1) to clear
     bool eager_clear = false;                     // the reserved cells are cleared by this call, eagerly
@@ -2741,7 +2729,7 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
             if (opt->workspace_bytes < wl.total) return DS_ERR_WORKSPACE;
             ws = opt->workspace;
         } else {
-            ws_lock = std::unique_lock<std::mutex>(g_ws_mu);
+            ws_lock = std::unique_lock<std::mutex>(g_ws.mu());
             if ((st = library_workspace(dev, hs, wl.total, &ws, &ws_zeroed)) != DS_OK) return st;
         }
         if (share) {
@@ -2887,12 +2875,6 @@ const char* deepselect_status_string(int status) {
     }
 }
 
-void deepselect_release(void) {
-    std::lock_guard<std::mutex> lk(ds::g_ws_mu);
-    for (auto& kv : ds::g_ws) {
-        if (kv.second.ptr) (void)hipFree(kv.second.ptr);
-    }
-    ds::g_ws.clear();
-}
+void deepselect_release(void) { ds::g_ws.release_all(ds::g_ws_ops); }
 
 }  // extern "C"
