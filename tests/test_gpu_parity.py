@@ -612,6 +612,62 @@ def test_fused_sampling_infinite_maximum(dt):
     assert np.all(np.isfinite(probs))
 
 
+# ---------------------------------------------------------------- merge: parts that cannot contribute
+
+def skew_rows(pattern, rows, n, dt, rng):
+    """Rows whose large values sit in chosen parts: ascending (only the last
+    part can contribute to the merge), descending (only the first), two
+    bumps (two parts), or Gaussian (every part)."""
+    i = np.arange(n, dtype=np.float64)
+    out = np.empty((rows, n), dtype=np.float64)
+    for r in range(rows):
+        noise = rng.standard_normal(n)
+        if pattern == "ascending":
+            out[r] = i / n * 100.0 + 1e-3 * noise
+        elif pattern == "descending":
+            out[r] = (n - i) / n * 100.0 + 1e-3 * noise
+        elif pattern == "two_bumps":
+            out[r] = noise
+            out[r, n // 8: n // 8 + n // 16] += 50.0
+            out[r, 6 * n // 8: 6 * n // 8 + n // 16] += 50.0
+        else:
+            out[r] = noise
+    x = out.astype(np.float32)
+    return x if dt == "f32" else synth.f32_to_bf16_bits(x)
+
+
+MERGE_SKIP = [(dt, pattern, split) for dt in ("f32", "bf16") for pattern in
+              ("ascending", "descending", "two_bumps", "gauss") for split in (8, 32)]
+
+
+@pytest.mark.parametrize("dt,pattern,split", MERGE_SKIP, ids=[f"{c[0]}-{c[1]}-S{c[2]}" for c in MERGE_SKIP])
+def test_merge_skips_parts_that_cannot_contribute(dt, pattern, split):
+    # the merge counts a part whose largest key is below t0 as empty without
+    # reading it, and with at most one contributing part builds no order: the
+    # results and the statistics are the model's either way
+    rng = np.random.default_rng(4242)
+    n, k, B = 16384, 512, 256
+    x = skew_rows(pattern, 2, n, dt, rng)
+    log(f"[gpu] merge skip {dt} {pattern} split {split}")
+    vals, idx, st = run_gpu(x, k, B, B, seed=5, split=split)
+    check_rows(x, vals, idx, k)
+    check_stats_against_model(x, st, k, B, B, 5, split, range(x.shape[0]))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_merge_skip_with_lengths(dt):
+    # ascending rows cut short: no part with k results (t0 = 0, every part
+    # with results admits), one part with results, or several
+    rng = np.random.default_rng(4243)
+    n, k, B, split = 16384, 512, 256, 16
+    x = skew_rows("ascending", 5, n, dt, rng)
+    lengths = np.asarray([100, 700, 3000, 9000, n], dtype=np.int32)
+    log(f"[gpu] merge skip with lengths {dt}")
+    vals, idx, st = run_gpu_len(x, k, B, B, lengths, seed=6, split=split)
+    check_rows_len(x, vals, idx, k, lengths)
+    check_stats_len(x, st, k, B, B, 6, split, lengths, range(x.shape[0]))
+
+
 # ---------------------------------------------------------------- shared thresholds
 
 SHARE = [
