@@ -28,11 +28,12 @@
 //     workgroup shares each block, one barrier per 4 KiB tile;
 //   * split rows (the deep-dive's "实现" section, last paragraph: a row cut into
 //     parts whose top-k go to one reducer): each part writes its results, their
-//     count and its k-th key to a device workspace; a second kernel, queued
-//     behind the first on the same stream, runs DeepSelect over the parts'
-//     results (one block per part) and writes the row. The kernel boundary
-//     makes the parts' writes visible, so no device-wide fence or arrival
-//     counter is needed;
+//     count, its k-th and its largest key to a device workspace; a second
+//     kernel, queued behind the first on the same stream, runs DeepSelect over
+//     the parts' results (one block per part, parts whose largest key cannot
+//     reach the row's top k counted empty without being read) and writes the
+//     row. The kernel boundary makes the parts' writes visible, so no
+//     device-wide fence or arrival counter is needed;
 //   * the kernel that writes a row can sort its results (a bitonic network in
 //     registers and LDS), take a softmax and draw a sample from them; rows may
 //     have their own valid lengths; the parts of a split row may share their
