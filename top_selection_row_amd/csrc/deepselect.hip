@@ -1951,46 +1951,41 @@ __global__ __launch_bounds__(kGW * 64) void deepselect_generic_kernel(Params p) 
 // ===========================================================================
 constexpr int kMT = 4;
 
+// A tile as loaded: the words are unpacked where they are used, so that the
+// wait for the loads falls there (after the work placed in between), not at
+// the loads. Entries past the part's k slots hold a copy of its last slot;
+// every use checks an entry against the part's count first.
+template <bool kPkParts>
 struct MergeTile {
-    uint32_t key[kMT], col[kMT];
+    uint32_t w[kMT], c[kMT];
+    uint32_t col0;  // packed words: the part's first column
+    __device__ __forceinline__ uint32_t key(int q) const { return kPkParts ? w[q] >> 16 : w[q]; }
+    __device__ __forceinline__ uint32_t col(int q) const { return kPkParts ? col0 + (w[q] & 0xFFFFu) : c[q]; }
 };
 
 // Tile t of part `part`'s results (lanes contiguous per load). kPkParts:
 // the parts wrote packed bfloat16 words, key << 16 | column inside the part,
-// whose first column is added back here.
+// whose first column is added back where the column is used.
 template <int NW, bool kPkParts>
-__device__ __forceinline__ void load_part_tile(MergeTile& t, const Params& p, int64_t row, int64_t part,
+__device__ __forceinline__ void load_part_tile(MergeTile<kPkParts>& t, const Params& p, int64_t row, int64_t part,
                                                uint32_t tile) {
     constexpr uint32_t TE = NW * 64 * kMT;
     const uint32_t k = (uint32_t)p.k;
     const uint32_t t0 = tile * TE;
     const int64_t off = (row * p.split + part) * (int64_t)k + t0;
-    uint32_t col0 = 0;
+    t.col0 = 0;
     if constexpr (kPkParts) {
         const int64_t m = p.lengths ? ceil_div(row_len(p, row), (int64_t)p.B) : p.m;
-        col0 = (uint32_t)(part_begin(m, part, p.split) * p.B);
+        t.col0 = (uint32_t)(part_begin(m, part, p.split) * p.B);
     }
     // unconditional loads at an index clamped into the part's slots (a
     // conditional load would be waited for before the next is issued)
-    uint32_t w[kMT], c[kMT];
 #pragma unroll
     for (int q = 0; q < kMT; ++q) {
         const uint32_t e = (uint32_t)q * NW * 64 + (uint32_t)threadIdx.x;
         const int64_t at = off + (t0 + e < k ? e : k - 1u - t0);
-        w[q] = p.ws_keys[at];
-        if constexpr (!kPkParts) c[q] = p.ws_idx[at];
-    }
-#pragma unroll
-    for (int q = 0; q < kMT; ++q) {
-        const uint32_t e = (uint32_t)q * NW * 64 + (uint32_t)threadIdx.x;
-        const bool inb = t0 + e < k;
-        if constexpr (kPkParts) {
-            t.key[q] = inb ? w[q] >> 16 : 0u;
-            t.col[q] = col0 + (w[q] & 0xFFFFu);
-        } else {
-            t.key[q] = inb ? w[q] : 0u;
-            t.col[q] = inb ? c[q] : 0u;
-        }
+        t.w[q] = p.ws_keys[at];
+        if constexpr (!kPkParts) t.c[q] = p.ws_idx[at];
     }
 }
 
@@ -2161,7 +2156,7 @@ __device__ __forceinline__ int32_t merge_bulk(Lds<D>& s, RunState& st, const Par
 // Tile number `tile` of the merge: tile tile % tpp of the part at order
 // position tile / tpp.
 template <int NW, bool kPkParts>
-__device__ __forceinline__ void load_merge_tile(MergeTile& t, const Params& p, const uint16_t* perm, int64_t row,
+__device__ __forceinline__ void load_merge_tile(MergeTile<kPkParts>& t, const Params& p, const uint16_t* perm, int64_t row,
                                                 int64_t tile, uint32_t tpp) {
     const int64_t i = tile / tpp;
     load_part_tile<NW, kPkParts>(t, p, row, (int64_t)uniform(perm[i]), (uint32_t)(tile - i * tpp));
@@ -2181,28 +2176,34 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
     const bool both = tiles == 2 && tpp == 1;
     uint32_t* pcnt = reinterpret_cast<uint32_t*>(smem + p.L.pcnt);
     for (int64_t row = blockIdx.x; row < p.batch; row += gridDim.x) {
-        MergeTile cur, nxt, pre0, pre1;
-        if (both) {
-            load_part_tile<NW, kPkParts>(pre0, p, row, 0, 0);
-            load_part_tile<NW, kPkParts>(pre1, p, row, 1, 0);
-        }
-        // the parts' result counts (short or filtered parts), lane q holding
-        // part q's, loaded with the first tiles (more than 64 parts: read
-        // where needed)
+        // The loads the row's start waits for come first, the first tiles
+        // after them: a wait for a load also waits for every load issued
+        // before it.
+        // The parts' result counts (short or filtered parts), lane q holding
+        // part q's (more than 64 parts: read where needed),
         const bool counted = p.lengths || p.ws_share;
         uint32_t part_cnt = k, part_max = 0xFFFFFFFFu;
         if (counted && S <= 64 && lane_id() < S) part_cnt = p.ws_cnt[row * S + lane_id()];
-        // and their largest keys: a part whose largest key is below the
-        // admission bound (t0 below) admits nothing, so its results are not
-        // read in the bulk phase
+        // their largest keys (a part whose largest key is below the
+        // admission bound t0 admits nothing, so its results are not read in
+        // the bulk phase),
         if (!both && S <= 64 && lane_id() < S) part_max = p.ws_tmax[row * S + lane_id()];
-        // the largest k-th key of the parts that hold k results: the k-th of
-        // any k elements of the row is at most the row's, so the merge admits
-        // only results at or above it (T starts just below it)
+        // and the largest k-th key of the parts that hold k results: the k-th
+        // of any k elements of the row is at most the row's, so the merge
+        // admits only results at or above it (T starts just below it).
         uint32_t t0 = 0;
-        for (int32_t q = lane_id(); q < S; q += 64) {
-            const uint32_t t = p.ws_tkey[row * S + q];
-            t0 = t > t0 ? t : t0;
+        if (S <= 64) {
+            if (lane_id() < S) t0 = p.ws_tkey[row * S + lane_id()];
+        } else {
+            for (int32_t q = lane_id(); q < S; q += 64) {
+                const uint32_t t = p.ws_tkey[row * S + q];
+                t0 = t > t0 ? t : t0;
+            }
+        }
+        MergeTile<kPkParts> cur, nxt, pre0, pre1;
+        if (both) {
+            load_part_tile<NW, kPkParts>(pre0, p, row, 0, 0);
+            load_part_tile<NW, kPkParts>(pre1, p, row, 1, 0);
         }
         t0 = wave_max(t0);
         // the previous row's final select has ended, so the histogram and the
@@ -2282,9 +2283,9 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
                 for (int q = 0; q < kMT; ++q) {
                     const uint32_t e = (uint32_t)q * NW * 64 + (uint32_t)threadIdx.x;
                     if (e < tv) {
-                        s.keys[st.len + e] = (typename D::Key)cur.key[q];
-                        s.idx[st.len + e] = cur.col[q];
-                        kmax = cur.key[q] > kmax ? cur.key[q] : kmax;
+                        s.keys[st.len + e] = (typename D::Key)cur.key(q);
+                        s.idx[st.len + e] = cur.col(q);
+                        kmax = cur.key(q) > kmax ? cur.key(q) : kmax;
                     }
                 }
                 st.len += tv;
@@ -2295,14 +2296,14 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
 #pragma unroll
                 for (int q = 0; q < kMT; ++q) {
                     const uint32_t e = (uint32_t)q * NW * 64 + (uint32_t)threadIdx.x;
-                    pred[q] = e < tv && cur.key[q] > st.tkey;
+                    pred[q] = e < tv && cur.key(q) > st.tkey;
                     masks[q] = __ballot(pred[q]);
                 }
                 const uint32_t added =
                     append_masked<NW, kMT>(masks, pred, st.len, s.cnt, st.par, [&](int q, uint32_t pos) {
-                        s.keys[pos] = (typename D::Key)cur.key[q];
-                        s.idx[pos] = cur.col[q];
-                        kmax = cur.key[q] > kmax ? cur.key[q] : kmax;
+                        s.keys[pos] = (typename D::Key)cur.key(q);
+                        s.idx[pos] = cur.col(q);
+                        kmax = cur.key(q) > kmax ? cur.key(q) : kmax;
                     });
                 st.len += added;
                 st.A += added;
