@@ -668,6 +668,45 @@ def test_merge_skip_with_lengths(dt):
     check_stats_len(x, st, k, B, B, 6, split, lengths, range(x.shape[0]))
 
 
+# ---------------------------------------------------------------- merge of two parts in registers
+
+MERGE_PAIR = [
+    # (dtype, k, B, B2, pattern): two parts of one merge tile each
+    ("bf16", 2048, 2048, 2048, "gauss"),     # the long-context shape
+    ("bf16", 2048, 2048, 512, "ties"),       # B2 < k: the merge's own compaction can trigger
+    ("f32", 512, 1024, 256, "ties"),
+    ("f32", 1024, 1024, 1024, "gauss"),
+    ("f32", 300, 256, 100, "gauss"),         # k not a multiple of 64
+    ("bf16", 1, 64, 1, "ties"),
+    ("f32", 512, 1024, 1024, "ascending"),   # only the second part admits results
+    ("bf16", 777, 512, 333, "descending"),   # only the first: no select in the merge
+]
+
+
+@pytest.mark.parametrize("dt,k,B,B2,pattern", MERGE_PAIR, ids=[f"{c[0]}-k{c[1]}-B2{c[3]}-{c[4]}" for c in MERGE_PAIR])
+def test_merge_of_two_parts_in_registers(dt, k, B, B2, pattern):
+    # the two-part merge with unsorted output runs in registers; the sorted
+    # output takes the tile loop and the candidate buffer, which keep the
+    # same results (ties included): the index sets must agree row by row, and
+    # both must agree with the oracle and the model's statistics
+    rng = np.random.default_rng(9090)
+    n, rows = 16384, 6
+    if pattern == "ties":
+        x32 = (rng.integers(0, 16, size=(rows, n)).astype(np.float32) * 0.5 - 3.0)
+        x = x32 if dt == "f32" else synth.f32_to_bf16_bits(x32)
+    else:
+        x = skew_rows(pattern, rows, n, dt, rng)
+    log(f"[gpu] two-part merge {dt} k {k} B {B} B2 {B2} {pattern}")
+    vals, idx, st = run_gpu(x, k, B, B2, seed=9, split=2)
+    check_rows(x, vals, idx, k)
+    check_stats_against_model(x, st, k, B, B2, 9, 2, range(rows))
+    s_vals, s_idx, s_st = run_gpu(x, k, B, B2, seed=9, split=2, sorted=True)
+    check_sorted_rows(x, s_vals, s_idx, k)
+    assert np.array_equal(st, s_st)
+    for r in range(rows):
+        assert np.array_equal(np.sort(idx[r]), np.sort(s_idx[r])), f"row {r}: kept set differs from the loop's"
+
+
 # ---------------------------------------------------------------- shared thresholds
 
 SHARE = [

@@ -1496,6 +1496,18 @@ __device__ __forceinline__ void write_sorted(Lds<D>& s, const Params& p, int64_t
     }
 }
 
+// A row's statistics, when asked for (thread 0 writes them).
+__device__ __forceinline__ void write_stats(const Params& p, int64_t row, uint64_t W, uint64_t A, uint64_t R,
+                                            uint64_t maxlen) {
+    if (p.stats && threadIdx.x == 0) {
+        uint64_t* o = p.stats + row * DS_STATS_PER_ROW;
+        o[DS_STAT_W] = W;
+        o[DS_STAT_A] = A;
+        o[DS_STAT_R] = R;
+        o[DS_STAT_MAX_LEN] = maxlen;
+    }
+}
+
 // Write a row's results: the cnt entries of the candidate buffer (cnt = k
 // unless the row's valid length is below k), then k - cnt fillers.
 template <class D, int NW>
@@ -1553,13 +1565,7 @@ __device__ __forceinline__ void write_row(Lds<D>& s, const Params& p, int64_t ro
         }
     }
     }
-    if (p.stats && threadIdx.x == 0) {
-        uint64_t* o = p.stats + row * DS_STATS_PER_ROW;
-        o[DS_STAT_W] = W;
-        o[DS_STAT_A] = A;
-        o[DS_STAT_R] = R;
-        o[DS_STAT_MAX_LEN] = maxlen;
-    }
+    write_stats(p, row, W, A, R, maxlen);
 }
 
 // Part results of split rows go to the workspace for the merge kernel.
@@ -2162,6 +2168,149 @@ __device__ __forceinline__ void load_merge_tile(MergeTile<kPkParts>& t, const Pa
     load_part_tile<NW, kPkParts>(t, p, row, (int64_t)uniform(perm[i]), (uint32_t)(tile - i * tpp));
 }
 
+// The merge of two parts of one tile each, held in registers (unsorted
+// output, every part holding k results): each thread keeps the results of
+// its slots of both tiles, the radix select counts them there, and the kept
+// ones go straight to the output, with no candidate buffer in LDS. What it
+// keeps, where each result lands in the output and the statistics are those
+// of the tile loop: the buffer order it stands for is (part in the row's
+// order, wave, slot, lane), and the one compaction check that can trigger
+// (after the second part) is counted as the loop counts it.
+// LDS: misc[8, 32) and tot[0, 4 NW) for the exchanges, the histogram copies
+// (clear on entry and on return).
+template <class D, int NW, bool kPkParts>
+__device__ __forceinline__ void merge_pair_regs(Lds<D>& s, RunState& st, const Params& p, int64_t row,
+                                                const MergeTile<kPkParts>& ta, const MergeTile<kPkParts>& tb) {
+    constexpr int E = 2 * kMT;
+    const uint32_t k = (uint32_t)p.k, B2 = (uint32_t)p.B2;
+    const int w = wave_id(), lane = lane_id();
+    uint32_t key[E];
+    uint64_t adm[E];  // the admitted results of each slot
+    uint32_t c[2] = {0u, 0u}, kmax = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int q = e % kMT;
+        key[e] = e < kMT ? ta.key(q) : tb.key(q);
+        const bool in = (uint32_t)q * NW * 64 + threadIdx.x < k && (!st.tset || key[e] > st.tkey);
+        adm[e] = __ballot(in);
+        kmax = in && key[e] > kmax ? key[e] : kmax;
+        c[e / kMT] += (uint32_t)__popcll(adm[e]);
+    }
+    kmax = wave_max(kmax);
+    if (lane == 0) {
+        s.misc[8 + w] = kmax;
+        s.misc[16 + w] = c[0];
+        s.misc[24 + w] = c[1];
+    }
+    lds_barrier();
+    uint32_t hi = 0, len0 = 0, len1 = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+        hi = s.misc[8 + v] > hi ? s.misc[8 + v] : hi;
+        len0 += s.misc[16 + v];
+        len1 += s.misc[24 + v];
+    }
+    hi = uniform(hi);
+    const uint32_t len = uniform(len0 + len1);
+    // the statistics of the tile loop and the final select
+    st.A += len;
+    st.maxlen = len > st.maxlen ? len : st.maxlen;
+    if (len >= k + B2) {
+        st.R += 1;
+        st.W += len + k;
+    } else {
+        st.W += len;
+    }
+    // the k-th key and the number of results equal to it that are kept
+    // (with no more than k admitted, all of them are kept)
+    uint32_t kth = 0, need = 0;
+    const bool sel = len > k;
+    if (sel) {
+        const uint32_t lo = st.tset ? st.tkey : 0u;
+        uint32_t base = lo, span = (hi > lo ? hi : lo) - lo, rank = k;
+        int sh = span ? 32 - __clz(span) : 0;
+        sh = sh > 8 ? sh - 8 : 0;
+        uint32_t* hl = s.hist + (lane & (kHistCopies - 1));
+        bool first = true;
+        while (true) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const uint32_t u = key[e] - base;
+                const bool in = ((adm[e] >> lane) & 1ull) && (first || u <= span);
+                uint32_t* at = &hl[__builtin_amdgcn_ubfe(u, (uint32_t)(sh + 1), 7u) * kHistCopies];
+                const uint32_t inc = 1u + __builtin_amdgcn_ubfe(u, (uint32_t)sh, 1u) * 0xFFFFu;
+                atomicAdd(at, in ? inc : 0u);
+            }
+            first = false;
+            lds_barrier();
+            fold_pass<NW>(s.hist, s.fold);
+            lds_barrier();
+            uint32_t cnt;
+            base += pick_bin(s.fold, rank, cnt) << sh;
+            if (sh == 0) break;
+            span = (1u << sh) - 1u;
+            sh = sh > 8 ? sh - 8 : 0;
+        }
+        kth = base;
+        need = rank;
+    }
+    // the kept results: every one above the k-th key and the first `need`
+    // equal to it, in buffer order; per wave and part, the number above and
+    // the number equal
+    uint64_t gt[E], eq[E];
+    uint32_t g[2] = {0u, 0u}, t[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const bool in = (adm[e] >> lane) & 1ull;
+        gt[e] = sel ? __ballot(in && key[e] > kth) : adm[e];
+        eq[e] = sel ? __ballot(in && key[e] == kth) : 0ull;
+        g[e / kMT] += (uint32_t)__popcll(gt[e]);
+        t[e / kMT] += (uint32_t)__popcll(eq[e]);
+    }
+    if (lane == 0) {
+        s.tot[w] = g[0];
+        s.tot[NW + w] = t[0];
+        s.tot[2 * NW + w] = g[1];
+        s.tot[3 * NW + w] = t[1];
+    }
+    lds_barrier();
+    // the results above and equal before this wave's block of each part
+    uint32_t gb[2] = {0u, 0u}, tb_[2] = {0u, 0u}, gall0 = 0, tall0 = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+        const uint32_t g0 = s.tot[v], t0 = s.tot[NW + v], g1 = s.tot[2 * NW + v], t1 = s.tot[3 * NW + v];
+        gall0 += g0;
+        tall0 += t0;
+        gb[0] += v < w ? g0 : 0u;
+        tb_[0] += v < w ? t0 : 0u;
+        gb[1] += v < w ? g1 : 0u;
+        tb_[1] += v < w ? t1 : 0u;
+    }
+    gb[1] += gall0;
+    tb_[1] += tall0;
+    uint32_t out = 0, seen = 0;  // kept results and equal results of this block before the slot
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int a = e / kMT, q = e % kMT;
+        if (q == 0) {
+            out = uniform(gb[a] + (tb_[a] < need ? tb_[a] : need));
+            seen = uniform(tb_[a]);
+        }
+        // the equal results of the slot that are kept: the first need - seen
+        const uint32_t left = seen < need ? need - seen : 0u;
+        const bool tie = (eq[e] >> lane) & 1ull;
+        const uint64_t kt = __ballot(tie && lanes_below(eq[e]) < left);
+        const uint64_t km = gt[e] | kt;
+        if ((km >> lane) & 1ull) {
+            const MergeTile<kPkParts>& tt = e < kMT ? ta : tb;
+            put_out<D>(p, row, out + lanes_below(km), D::raw(key[e]), (int32_t)tt.col(q));
+        }
+        out += (uint32_t)__popcll(km);
+        seen += (uint32_t)__popcll(eq[e]);
+    }
+    st.len = sel ? k : len;
+}
+
 template <class D, int NW, bool kPkParts>
 __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -2227,8 +2376,11 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
             cur = swap ? pre1 : pre0;
             nxt = swap ? pre0 : pre1;
         }
+        // two parts of one tile, each holding k results, unsorted output: the
+        // merge runs in registers (merge_pair_regs), not through the loop
+        const bool regs = both && !counted && !p.sorted;
         int64_t j0 = 0;          // the first tile the part-by-part loop takes
-        int64_t tiles_end = tiles;  // and the end
+        int64_t tiles_end = regs ? 0 : tiles;  // and the end
         // At most one part that can admit results (a part admits none when
         // its largest key is below t0, or it has none): the order of the
         // parts changes neither the buffer nor the statistics, so no order
@@ -2316,7 +2468,10 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
             cur = nxt;
         }
         DS_PROF(st, 3);
-        final_select<D, NW>(s, st, k);
+        if (regs)
+            merge_pair_regs<D, NW, kPkParts>(s, st, p, row, cur, nxt);
+        else
+            final_select<D, NW>(s, st, k);
         DS_PROF(st, 4);
         // the parts' statistics: lane q takes parts q, q + 64, ..., then the
         // wave adds them up (only when asked for)
@@ -2343,7 +2498,10 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
         R += st.R;
         maxlen = st.maxlen > maxlen ? st.maxlen : maxlen;
         DS_PROF(st, 5);
-        write_row<D, NW>(s, p, row, st.len, W, A, R, maxlen);
+        if (regs)
+            write_stats(p, row, W, A, R, maxlen);
+        else
+            write_row<D, NW>(s, p, row, st.len, W, A, R, maxlen);
         // every part of the row has ended (the part kernel came before): its
         // shared threshold cell is left zero for the next call
         if (p.ws_share && threadIdx.x == 0) p.ws_share[row * kCellWords] = 0u;
