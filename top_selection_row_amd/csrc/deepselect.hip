@@ -2170,14 +2170,14 @@ __device__ __forceinline__ void load_merge_tile(MergeTile<kPkParts>& t, const Pa
 
 // The merge of two parts of one tile each, held in registers (unsorted
 // output, every part holding k results): each thread keeps the results of
-// its slots of both tiles, the radix select counts them there, and the kept
-// ones go straight to the output, with no candidate buffer in LDS. What it
-// keeps, where each result lands in the output and the statistics are those
-// of the tile loop: the buffer order it stands for is (part in the row's
-// order, wave, slot, lane), and the one compaction check that can trigger
-// (after the second part) is counted as the loop counts it.
-// LDS: misc[8, 32) and tot[0, 4 NW) for the exchanges, the histogram copies
-// (clear on entry and on return).
+// its slots of both tiles, the radix select counts them there, and only the
+// kept ones are stored, in output order, to the front of the candidate
+// buffer (write_row copies them out). What it keeps, where each result lands
+// and the statistics are those of the tile loop: the buffer order it stands
+// for is (part in the row's order, wave, slot, lane), and the one compaction
+// check that can trigger (after the second part) is counted as the loop
+// counts it. LDS: misc[8, 32) and tot[0, 4 NW) for the exchanges, the
+// histogram copies (clear on entry and on return); ends with a barrier.
 template <class D, int NW, bool kPkParts>
 __device__ __forceinline__ void merge_pair_regs(Lds<D>& s, RunState& st, const Params& p, int64_t row,
                                                 const MergeTile<kPkParts>& ta, const MergeTile<kPkParts>& tb) {
@@ -2299,16 +2299,19 @@ __device__ __forceinline__ void merge_pair_regs(Lds<D>& s, RunState& st, const P
         // the equal results of the slot that are kept: the first need - seen
         const uint32_t left = seen < need ? need - seen : 0u;
         const bool tie = (eq[e] >> lane) & 1ull;
-        const uint64_t kt = __ballot(tie && lanes_below(eq[e]) < left);
+        const uint64_t kt = __ballot(tie & (lanes_below(eq[e]) < left));
         const uint64_t km = gt[e] | kt;
         if ((km >> lane) & 1ull) {
             const MergeTile<kPkParts>& tt = e < kMT ? ta : tb;
-            put_out<D>(p, row, out + lanes_below(km), D::raw(key[e]), (int32_t)tt.col(q));
+            const uint32_t at = out + lanes_below(km);
+            s.keys[at] = (typename D::Key)key[e];
+            s.idx[at] = tt.col(q);
         }
         out += (uint32_t)__popcll(km);
         seen += (uint32_t)__popcll(eq[e]);
     }
     st.len = sel ? k : len;
+    lds_barrier();  // the kept results, in output order, are visible to write_row
 }
 
 template <class D, int NW, bool kPkParts>
@@ -2498,10 +2501,7 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
         R += st.R;
         maxlen = st.maxlen > maxlen ? st.maxlen : maxlen;
         DS_PROF(st, 5);
-        if (regs)
-            write_stats(p, row, W, A, R, maxlen);
-        else
-            write_row<D, NW>(s, p, row, st.len, W, A, R, maxlen);
+        write_row<D, NW>(s, p, row, st.len, W, A, R, maxlen);
         // every part of the row has ended (the part kernel came before): its
         // shared threshold cell is left zero for the next call
         if (p.ws_share && threadIdx.x == 0) p.ws_share[row * kCellWords] = 0u;
