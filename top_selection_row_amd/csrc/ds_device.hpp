@@ -156,15 +156,22 @@ __device__ void build_order(uint16_t* perm, uint64_t seed, int64_t row, int tag,
             rank[t] = 0u;
         }
         lds_barrier();
-        const int lo = wave * count / NW, hi = (wave + 1) * count / NW;
-        for (int j = lane; j < count; j += 64) {
-            const uint64_t h = hk[j];
+        // the wave's slice (at most 64 ids) sits one hash a lane, and each
+        // is read back by a lane read, not a dependent LDS read per compare
+        const int lo = (int)uniform((uint32_t)(wave * count / NW));
+        const int n = (int)uniform((uint32_t)((wave + 1) * count / NW)) - lo;
+        const uint64_t mine = lane < n ? hk[lo + lane] : 0ull;
+        const uint32_t m_lo = (uint32_t)mine, m_hi = (uint32_t)(mine >> 32);
+        for (int j0 = 0; j0 < count; j0 += 64) {
+            const int j = j0 + lane;
+            const uint64_t h = j < count ? hk[j] : 0ull;
             uint32_t r = 0;
-            for (int i = lo; i < hi; ++i) {
-                const uint64_t o = hk[i];
-                r += (o < h) || (o == h && i < j);
+            for (int i = 0; i < n; ++i) {
+                const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)m_hi, i) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readlane((int)m_lo, i);
+                r += (o < h) || (o == h && lo + i < j);
             }
-            if (r) atomicAdd(&rank[j], r);
+            if (j < count && r) atomicAdd(&rank[j], r);
         }
         lds_barrier();
         if (t < count) perm[rank[t]] = (uint16_t)t;
