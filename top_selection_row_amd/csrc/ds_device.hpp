@@ -139,9 +139,9 @@ __device__ __forceinline__ uint64_t splitmix_at(uint64_t seed, uint64_t ctr) {
 
 // perm[i] = the i-th of `count` ids (0-based, relative to id0) in random order.
 // Every thread of the workgroup must call it; it ends with a barrier.
-// count <= 64*NW: rank counting -- wave w compares every id with the ids of its
-// slice of the list and adds the partial ranks into LDS; then perm[rank] = id.
-// Larger counts: a bitonic sort of (hash, id) pairs in LDS.
+// count <= 64*NW: rank counting -- thread t counts the hashes below id t's
+// and writes perm[rank] = t. Larger counts: a bitonic sort of (hash, id)
+// pairs in LDS.
 template <int NW>
 __device__ void build_order(uint16_t* perm, uint64_t seed, int64_t row, int tag, int64_t id0, int count,
                             unsigned char* scratch) {
@@ -150,31 +150,32 @@ __device__ void build_order(uint16_t* perm, uint64_t seed, int64_t row, int tag,
     const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
     uint64_t* hk = reinterpret_cast<uint64_t*>(scratch);
     if (count <= kLanes) {
-        uint32_t* rank = reinterpret_cast<uint32_t*>(scratch + (size_t)count * 8);
+        // Hashes of distinct ids differ (SplitMix64's state steps by an odd
+        // constant and each step of its mix is a bijection of 64-bit words),
+        // so an id's place is the number of smaller hashes: thread t counts
+        // them for id t over the whole list, read 8 hashes at a time (16-byte
+        // broadcast reads; the list is padded to a multiple of 8 with the
+        // largest word, which is smaller than no hash).
+        const int padded = (count + 7) & ~7;
+        const uint64_t h = t < count ? splitmix_at(seed, ctr0 + (uint64_t)t) : 0ull;
+        if (t < padded) hk[t] = t < count ? h : ~0ull;
+        lds_barrier();
         if (t < count) {
-            hk[t] = splitmix_at(seed, ctr0 + (uint64_t)t);
-            rank[t] = 0u;
-        }
-        lds_barrier();
-        // the wave's slice (at most 64 ids) sits one hash a lane, and each
-        // is read back by a lane read, not a dependent LDS read per compare
-        const int lo = (int)uniform((uint32_t)(wave * count / NW));
-        const int n = (int)uniform((uint32_t)((wave + 1) * count / NW)) - lo;
-        const uint64_t mine = lane < n ? hk[lo + lane] : 0ull;
-        const uint32_t m_lo = (uint32_t)mine, m_hi = (uint32_t)(mine >> 32);
-        for (int j0 = 0; j0 < count; j0 += 64) {
-            const int j = j0 + lane;
-            const uint64_t h = j < count ? hk[j] : 0ull;
+            const u32x4* hv = reinterpret_cast<const u32x4*>(hk);
             uint32_t r = 0;
-            for (int i = 0; i < n; ++i) {
-                const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)m_hi, i) << 32) |
-                                   (uint32_t)__builtin_amdgcn_readlane((int)m_lo, i);
-                r += (o < h) || (o == h && lo + i < j);
+            for (int i0 = 0; i0 < padded; i0 += 8) {
+                u32x4 v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = hv[i0 / 2 + q];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint64_t a = ((uint64_t)v[q].y << 32) | v[q].x;
+                    const uint64_t b = ((uint64_t)v[q].w << 32) | v[q].z;
+                    r += (a < h ? 1u : 0u) + (b < h ? 1u : 0u);
+                }
             }
-            if (j < count && r) atomicAdd(&rank[j], r);
+            perm[r] = (uint16_t)t;
         }
-        lds_barrier();
-        if (t < count) perm[rank[t]] = (uint16_t)t;
     } else {
         const int p2 = (int)next_pow2(count);
         uint32_t* hid = reinterpret_cast<uint32_t*>(scratch + (size_t)p2 * 8);
