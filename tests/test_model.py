@@ -44,6 +44,32 @@ def test_splitmix64_known_answer():
     assert [int(v) for v in got] == [int(h, 16) for h in g["outputs_hex"]]
 
 
+def test_splitmix64_outputs_of_distinct_counters_differ():
+    # the state steps by an odd constant and every step of the mix is a
+    # bijection of 64-bit words, so no two counters share an output: the
+    # block order never needs its id tie-break (the kernels rank ids by their
+    # hash alone); checked on a row's counter range for a few seeds and rows
+    for seed in (0, 1, 0xDEADBEEF, 2**64 - 1):
+        for row, tag in ((0, 0), (127, 1), (2**20, 0)):
+            ctr = np.uint64((row * 2 + tag) << 32) + np.arange(1 << 16, dtype=np.uint64)
+            h = model.splitmix64(seed, ctr)
+            assert len(np.unique(h)) == h.size
+    # and each mixing step inverts: z ^ (z >> s) is undone by the same
+    # shifts repeated, a product by an odd constant by its inverse mod 2^64
+    rng = np.random.default_rng(5)
+    z = rng.integers(0, 2**63, 1000, dtype=np.uint64) * np.uint64(2) + np.uint64(1)
+    for s_ in (30, 27, 31):
+        y = z ^ (z >> np.uint64(s_))
+        back = y.copy()
+        for _ in range(64 // s_ + 1):
+            back = y ^ (back >> np.uint64(s_))
+        assert np.array_equal(back, z)
+    for m in (model.MIX_M1, model.MIX_M2, model.GOLDEN_GAMMA):
+        inv = pow(int(m), -1, 2**64)
+        with np.errstate(over="ignore"):
+            assert np.array_equal(z * np.uint64(m) * np.uint64(inv), z)
+
+
 def test_radix_select_against_sorting():
     rng = np.random.default_rng(1)
     for bits in (16, 32):
