@@ -2413,13 +2413,27 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
             DS_PROF(st, 2);
             if (trig < S) compact<D, NW>(s, st, k);
             j0 = (int64_t)(trig + 1) * tpp;
-            if (j0 < tiles) load_merge_tile<NW, kPkParts>(cur, p, s.perm, row, j0, tpp);
         }
-        for (int64_t j = j0; j < tiles_end; ++j) {
+        // The tile to take after tile j - 1: a whole part whose largest key
+        // is at or below T admits nothing, so its tiles are not read (its
+        // compaction check would repeat the one before it). Decided with T
+        // as it stands when the tile is requested; a part T passes later is
+        // read and filters to nothing.
+        const auto next_tile = [&](int64_t j) -> int64_t {
+            if (single || both || S > 64) return j;
+            while (j < tiles && j % tpp == 0 && st.tset &&
+                   uniform(__builtin_amdgcn_readlane(part_max, (int)uniform(s.perm[j / tpp]))) <= st.tkey)
+                j += tpp;
+            return j;
+        };
+        j0 = next_tile(j0);
+        if (!single && !both && j0 < tiles) load_merge_tile<NW, kPkParts>(cur, p, s.perm, row, j0, tpp);
+        for (int64_t j = j0, jn = 0; j < tiles_end; j = jn) {
+            jn = next_tile(j + 1);
             if (single) {
-                if (j + 1 < tiles_end) load_part_tile<NW, kPkParts>(nxt, p, row, sid, (uint32_t)(j + 1));
-            } else if (!both && j + 1 < tiles) {
-                load_merge_tile<NW, kPkParts>(nxt, p, s.perm, row, j + 1, tpp);
+                if (jn < tiles_end) load_part_tile<NW, kPkParts>(nxt, p, row, sid, (uint32_t)jn);
+            } else if (!both && jn < tiles) {
+                load_merge_tile<NW, kPkParts>(nxt, p, s.perm, row, jn, tpp);
             }
             const uint32_t t0 = (uint32_t)(j % tpp) * TE;
             // results of the part: k, or fewer for a part shorter than k or
