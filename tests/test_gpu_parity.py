@@ -685,10 +685,11 @@ MERGE_PAIR = [
 
 @pytest.mark.parametrize("dt,k,B,B2,pattern", MERGE_PAIR, ids=[f"{c[0]}-k{c[1]}-B2{c[3]}-{c[4]}" for c in MERGE_PAIR])
 def test_merge_of_two_parts_in_registers(dt, k, B, B2, pattern):
-    # the two-part merge with unsorted output runs in registers; the sorted
-    # output takes the tile loop and the candidate buffer, which keep the
-    # same results (ties included): the index sets must agree row by row, and
-    # both must agree with the oracle and the model's statistics
+    # the two-part merge runs in registers (unsorted and sorted output);
+    # with valid lengths given (here the full rows) it takes the tile loop
+    # and the candidate buffer, which keep the same results (ties included):
+    # the index sets must agree row by row, and all must agree with the
+    # oracle and the model's statistics
     rng = np.random.default_rng(9090)
     n, rows = 16384, 6
     if pattern == "ties":
@@ -702,9 +703,12 @@ def test_merge_of_two_parts_in_registers(dt, k, B, B2, pattern):
     check_stats_against_model(x, st, k, B, B2, 9, 2, range(rows))
     s_vals, s_idx, s_st = run_gpu(x, k, B, B2, seed=9, split=2, sorted=True)
     check_sorted_rows(x, s_vals, s_idx, k)
-    assert np.array_equal(st, s_st)
+    l_vals, l_idx, l_st = run_gpu_len(x, k, B, B2, np.full(rows, n, dtype=np.int32), seed=9, split=2)
+    check_rows(x, l_vals, l_idx, k)
+    assert np.array_equal(st, s_st) and np.array_equal(st, l_st)
     for r in range(rows):
-        assert np.array_equal(np.sort(idx[r]), np.sort(s_idx[r])), f"row {r}: kept set differs from the loop's"
+        assert np.array_equal(np.sort(idx[r]), np.sort(s_idx[r])), f"row {r}: sorted kept set differs"
+        assert np.array_equal(np.sort(idx[r]), np.sort(l_idx[r])), f"row {r}: kept set differs from the loop's"
 
 
 # ---------------------------------------------------------------- shared thresholds
