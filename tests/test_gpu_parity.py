@@ -685,11 +685,11 @@ MERGE_PAIR = [
 
 @pytest.mark.parametrize("dt,k,B,B2,pattern", MERGE_PAIR, ids=[f"{c[0]}-k{c[1]}-B2{c[3]}-{c[4]}" for c in MERGE_PAIR])
 def test_merge_of_two_parts_in_registers(dt, k, B, B2, pattern):
-    # the two-part merge runs in registers (unsorted and sorted output);
-    # with valid lengths given (here the full rows) it takes the tile loop
-    # and the candidate buffer, which keep the same results (ties included):
-    # the index sets must agree row by row, and all must agree with the
-    # oracle and the model's statistics
+    # the two-part merge runs in registers for unsorted output; with sorted
+    # output, or valid lengths given (here the full rows), it takes the tile
+    # loop and the candidate buffer, which keep the same results (ties
+    # included): the index sets must agree row by row, and all must agree
+    # with the oracle and the model's statistics
     rng = np.random.default_rng(9090)
     n, rows = 16384, 6
     if pattern == "ties":

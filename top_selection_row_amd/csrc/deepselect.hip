@@ -2172,7 +2172,7 @@ __device__ __forceinline__ void load_merge_tile(MergeTile<kPkParts>& t, const Pa
 // holding k results): each thread keeps the results of its slots of both
 // tiles, the radix select counts them there, and only the kept ones are
 // stored, in output order, to the front of the candidate buffer (write_row
-// copies them out, or sorts them first). What it keeps, where each result lands
+// copies them out). What it keeps, where each result lands
 // and the statistics are those of the tile loop: the buffer order it stands
 // for is (part in the row's order, wave, slot, lane), and the one compaction
 // check that can trigger (after the second part) is counted as the loop
@@ -2379,9 +2379,11 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
             cur = swap ? pre1 : pre0;
             nxt = swap ? pre0 : pre1;
         }
-        // two parts of one tile, each holding k results: the merge runs in
-        // registers (merge_pair_regs), not through the loop
-        const bool regs = both && !counted;
+        // two parts of one tile, each holding k results, unsorted output: the
+        // merge runs in registers (merge_pair_regs), not through the loop
+        // (with sorted output too it gains 0.7 us on the sort's side and
+        // costs the unsorted call 0.4 us in the compiled merge)
+        const bool regs = both && !counted && !p.sorted;
         int64_t j0 = 0;          // the first tile the part-by-part loop takes
         int64_t tiles_end = regs ? 0 : tiles;  // and the end
         // At most one part that can admit results (a part admits none when
