@@ -99,9 +99,9 @@ typedef struct ds_options {
      * Size from deepselect_workspace_bytes; no initial contents are needed. It
      * holds every part's results (up to k), their count, the part's k-th and
      * largest keys and statistics between the part kernel and the merge
-     * kernel, and the
-     * rows' shared-threshold cells, so it must not be shared by calls that may
-     * overlap. */
+     * (the merge kernel, or for rows of two bfloat16 parts the part that ends
+     * last), and the rows' cells (shared thresholds and the count of a row's
+     * ended parts), so it must not be shared by calls that may overlap. */
     void *workspace;
     size_t workspace_bytes;
     /* Kernel: 0 = library choice; 1 = ring streaming (blocks copied HBM -> LDS
@@ -165,8 +165,11 @@ typedef struct ds_options {
      * part's k-th value is at most the row's, so the result set is the same;
      * the statistics then depend on timing (W = A + k*R still holds per row,
      * W counting the whole buffer at the final stage).
-     * The row cells (one uint64 per row, 128 bytes apart) must be zero when
-     * the parts start, and the merge kernel leaves them zero. The first 1024
+     * The row cells (128 bytes per row: the shared threshold in the first
+     * uint64, and in the ninth the count of the row's ended parts, which
+     * rows of two bfloat16 parts merged by their last part use) must be zero
+     * when the parts start; the merge kernel, or that last part, leaves them
+     * zero. The first 1024
      * cells sit at the start of a library-owned workspace or of the noalloc
      * scratch, where no other array overlaps them, so they are cleared only
      * once: by the first such call that is not under graph capture. Cells
@@ -201,8 +204,8 @@ int deepselect_topk_ex(const void *x, int dtype, int64_t batch, int64_t N, int64
  * keys, statistics and shared-threshold cells) lives in a static device array of
  * 8 MiB, one copy per GPU the library runs on, kept until the process ends;
  * its device address is looked up once per device on the first call there.
- * Its first 128 KiB hold 1024 reserved shared-threshold cells (see
- * share_threshold); deepselect_scratch_bytes() is the rest. Arguments and results are those of
+ * Its first 128 KiB hold 1024 reserved row cells (see share_threshold);
+ * deepselect_scratch_bytes() is the rest. Arguments and results are those of
  * deepselect_topk_ex with the same options, except:
  *   - opt->workspace must be NULL (else DS_ERR_SCRATCH);
  *   - a call whose split needs more workspace than the scratch holds

@@ -922,6 +922,66 @@ def test_graph_capture_replays(share):
         torch.cuda.synchronize()
 
 
+def test_merge_in_part_kernel_repeats_and_graph_replays():
+    # rows of two packed bfloat16 parts (unsorted) are merged by the part
+    # that ends last, after an arrival count in the row's cell that this part
+    # resets: repeated calls through the library workspace (batches on both
+    # sides), calls with a caller workspace and replays of a captured graph
+    # must give the first call's results and statistics, which match the
+    # oracle and the model
+    w = synth.WORKLOADS["dsa128k_bf16"]
+    rows, S, seed = 8, 2, 4
+    log(f"[gpu] merge in the part kernel: {rows} rows, split {S}")
+    x = synth.generate("dsa128k_bf16", rows)
+    vals, idx, st = run_gpu(x, w.k, w.block, w.block2, seed=seed, split=S)
+    check_rows(x, vals, idx, w.k)
+    check_stats_against_model(x, st, w.k, w.block, w.block2, seed, S, range(4))
+    for rep in range(3):
+        v3, i3, s3 = run_gpu(x[:3], w.k, w.block, w.block2, seed=seed, split=S)
+        assert np.array_equal(v3, vals[:3]) and np.array_equal(i3, idx[:3]) and np.array_equal(s3, st[:3])
+        v8, i8, s8 = run_gpu(x, w.k, w.block, w.block2, seed=seed, split=S)
+        assert np.array_equal(v8, vals) and np.array_equal(i8, idx) and np.array_equal(s8, st), f"repeat {rep}"
+    # a caller workspace, eagerly and captured
+    xt = to_device(x)
+    other = to_device(synth.generate("dsa128k_bf16", rows)[::-1].copy())
+    nbytes = ds.deepselect_workspace_bytes(ds.DS_BF16, rows, w.n, w.k, w.block, w.block2, S)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    gv = torch.empty((rows, w.k), dtype=torch.bfloat16, device=DEV)
+    gi = torch.empty((rows, w.k), dtype=torch.int32, device=DEV)
+    gs = torch.empty((rows, 4), dtype=torch.int64, device=DEV)
+    ov, oi = torch.empty_like(gv), torch.empty_like(gi)
+
+    def call(src, v, i, stream):
+        rc = ds.deepselect_topk_ex(src.data_ptr(), ds.DS_BF16, rows, w.n, w.n, w.k, w.block, w.block2, seed,
+                                   v.data_ptr(), i.data_ptr(), stream, split=S, stats=gs.data_ptr(),
+                                   workspace=ws.data_ptr(), workspace_bytes=nbytes)
+        assert rc == 0, ds.deepselect_status_string(rc)
+
+    cur = torch.cuda.current_stream().cuda_stream
+    call(xt, gv, gi, cur)
+    torch.cuda.synchronize()
+    assert np.array_equal(raw_of(gv), vals) and np.array_equal(gi.cpu().numpy(), idx)
+    assert np.array_equal(gs.cpu().numpy(), st)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(xt, gv, gi, side.cuda_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        call(xt, gv, gi, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        gv.zero_()
+        gi.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(raw_of(gv), vals) and np.array_equal(gi.cpu().numpy(), idx), f"replay {rep}"
+        assert np.array_equal(gs.cpu().numpy(), st), f"replay {rep}: statistics differ"
+        call(other, ov, oi, cur)
+        torch.cuda.synchronize()
+
+
 def test_two_streams_at_once():
     # split calls on two streams in flight together: each stream has its own
     # library workspace, so neither call sees the other's partial results

@@ -32,8 +32,11 @@
 //     kernel, queued behind the first on the same stream, runs DeepSelect over
 //     the parts' results (one block per part, parts whose largest key cannot
 //     reach the row's top k counted empty without being read) and writes the
-//     row. The kernel boundary makes the parts' writes visible, so no
-//     device-wide fence or arrival counter is needed;
+//     row. The kernel boundary makes the parts' writes visible. Rows of two
+//     bfloat16 parts (unsorted output) are merged instead by the part that
+//     ends last, after a device-scope acquire-release count of the row's
+//     ended parts: it starts as soon as its own select ends, not after the
+//     slowest part of every row, and no second kernel is launched;
 //   * the kernel that writes a row can sort its results (a bitonic network in
 //     registers and LDS), take a softmax and draw a sample from them; rows may
 //     have their own valid lengths; the parts of a split row may share their
@@ -82,6 +85,7 @@ struct Params {
     uint32_t* ws_cnt;        // per part: its number of results
     uint32_t* ws_tkey;       // per part: its k-th key when it has k results, else 0
     uint32_t* ws_tmax;       // per part: its largest result key (0 without results)
+    uint64_t* ws_arrive;     // per row: parts ended (word kArriveWord of its cell), or NULL: merge kernel
     Layout L;
 };
 
@@ -1027,6 +1031,29 @@ struct RingStreamer {
 template <class D, int NW, int U>
 __global__ __launch_bounds__(NW * 64) void deepselect_ring_kernel(Params p);
 
+// Rows of two parts merged inside the part kernel, by the part that ends
+// last. Each part has written its results, counts and statistics; after a
+// workgroup barrier (every thread's stores done) thread 0 counts the part in
+// the row's arrival word with a device-scope acquire-release add, which
+// publishes this workgroup's stores and, for the part that sees the other
+// part already counted, makes that part's stores visible to its loads. The
+// last part resets the word for the next call. Returns whether this part
+// merges the row (the same in every thread).
+__device__ __forceinline__ bool arrive_last(const Params& p, int64_t row, uint32_t* flag) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t* w = p.ws_arrive + row * kCellWords;
+        const uint64_t before = __hip_atomic_fetch_add(w, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = before + 1u == (uint64_t)p.split;
+        if (last) __hip_atomic_store(w, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = last ? 1u : 0u;
+    }
+    lds_barrier();
+    return uniform(*flag) != 0u;
+}
+template <int NW>
+__device__ void merge_in_part_kernel(unsigned char* smem, const Params& p, int64_t row);
+
 // Sorted output. Every result becomes one 64-bit word key << 32 | ~column,
 // so plain descending order of the words is the wanted one (keys from the
 // largest down, equal keys by ascending column); padding words are 0, below
@@ -1732,6 +1759,9 @@ __global__ __launch_bounds__(NW * 64) void deepselect_ring_kernel(Params p) {
         else
             write_part<D, NW>(s, st, p, g.slot, (uint32_t)g.part_elem0);
         DS_PROF(st, 12);
+        if constexpr (is_packed<D>::value) {
+            if (p.ws_arrive && arrive_last(p, g.row, s.misc + 4)) merge_in_part_kernel<NW>(smem, p, g.row);
+        }
 #ifdef DS_PROFILE
         st.prof_flush();
 #endif
@@ -2314,6 +2344,43 @@ __device__ __forceinline__ void merge_pair_regs(Lds<D>& s, RunState& st, const P
     lds_barrier();  // the kept results, in output order, are visible to write_row
 }
 
+// The two-part merge run by the part that ends last (packed bfloat16 parts,
+// unsorted output, every part holding k results, k at most a tile): the
+// merge kernel's register merge on an LDS view of the part kernel's layout
+// (16-bit keys in the candidate array, columns in the block ring, which both
+// hold nothing the part still needs), with the same statistics.
+template <int NW>
+__device__ void merge_in_part_kernel(unsigned char* smem, const Params& p, int64_t row) {
+    Lds<BF16T> m = lds_of<BF16T>(smem, p.L);
+    m.idx = reinterpret_cast<uint32_t*>(smem + p.L.ring);
+    uint32_t t0 = lane_id() < 2 ? p.ws_tkey[row * 2 + lane_id()] : 0u;
+    MergeTile<true> a, b;
+    load_part_tile<NW, true>(a, p, row, 0, 0);
+    load_part_tile<NW, true>(b, p, row, 1, 0);
+    t0 = wave_max(t0);
+    RunState st;
+    if (t0 != 0u) {
+        st.tset = st.fset = true;
+        st.tkey = st.fkey = t0 - 1u;
+    }
+    // the parts' order: (part 1, part 0) when part 1's hash is the smaller
+    const uint64_t ctr0 = (uint64_t)(row * 2 + 1) << 32;
+    const bool swap = splitmix_at(p.seed, ctr0 + 1u) < splitmix_at(p.seed, ctr0);
+    merge_pair_regs<BF16T, NW, true>(m, st, p, row, swap ? b : a, swap ? a : b);
+    uint64_t W = st.W, A = st.A, R = st.R, maxlen = st.maxlen;
+    if (p.stats) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint64_t* o = p.ws_stats + (row * 2 + q) * DS_STATS_PER_ROW;
+            W += o[DS_STAT_W];
+            A += o[DS_STAT_A];
+            R += o[DS_STAT_R];
+            maxlen = o[DS_STAT_MAX_LEN] > maxlen ? o[DS_STAT_MAX_LEN] : maxlen;
+        }
+    }
+    write_row<BF16T, NW>(m, p, row, st.len, W, A, R, maxlen);
+}
+
 template <class D, int NW, bool kPkParts>
 __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -2532,8 +2599,10 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
 // zero, before the parts start): a kernel, not a memset, so that the call
 // stays capturable.
 __global__ void deepselect_zero_kernel(uint64_t* p, int64_t n) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
         p[i * kCellWords] = 0u;
+        p[i * kCellWords + kArriveWord] = 0u;
+    }
 }
 
 // ===========================================================================
@@ -2725,7 +2794,7 @@ static int launch_all(KernelKind kind, int units, int waves, bool vec, Params pr
         else
             rc = launch_kernel(deepselect_generic_kernel<D, false>, items, kGW * 64, lds, st, prm);
     }
-    if (rc != DS_OK || prm.split == 1) return rc;
+    if (rc != DS_OK || prm.split == 1 || prm.ws_arrive) return rc;
     // the merge runs on 8 waves when a part's k results need more than one
     // tile of 4 waves, or when 16 parts or more are counted at its start, and
     // the layout fits, else on 4 (measured: 8 waves are 2 us faster at
@@ -2879,6 +2948,11 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     // two steps after it goes out): parts with fewer steps run as without it.
     const bool share = share_req && S > 1 && kind == kRing &&
                        ceil_div(ceil_div(ceil_div(n, B), S), waves) >= kShareMinSteps;
+    // Rows of two packed bfloat16 parts whose k results fit one merge tile,
+    // unsorted, with every part holding k results: the part that ends last
+    // merges the row (an arrival count per row in its cell), no merge kernel.
+    const bool fuse = S == 2 && kind == kRing && packed && (int64_t)k <= (int64_t)waves * 64 * 4 && !sorted &&
+                      !sampling && !(opt && opt->lengths) && !share;
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     std::unique_lock<std::mutex> ws_lock;  // held while a library workspace is in use
@@ -2893,6 +2967,7 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     std::atomic<bool>* sc_zeroed = nullptr;       // scratch
     int64_t clear0 = 0, clear1 = 0;               // cells [clear0, clear1) to clear
     bool eager_clear = false;                     // the reserved cells are cleared by this call, eagerly
+    uint64_t* cells = nullptr;                    // the rows' cells
     if (S > 1) {
         const bool own = noalloc || !(opt && opt->workspace);
         const WsLayout wl = make_ws_layout(batch, k, S, own ? kCells : 0);
@@ -2908,7 +2983,7 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
             ws_lock = std::unique_lock<std::mutex>(g_ws.mu());
             if ((st = library_workspace(dev, hs, wl.total, &ws, &ws_zeroed)) != DS_OK) return st;
         }
-        if (share) {
+        if (share || fuse) {
             clear1 = batch;
             if (own) {
                 const bool zeroed = ws_zeroed ? *ws_zeroed : sc_zeroed->load();
@@ -2928,13 +3003,15 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
         prm.ws_cnt = reinterpret_cast<uint32_t*>(w + wl.cnt);
         prm.ws_tkey = reinterpret_cast<uint32_t*>(w + wl.tkey);
         prm.ws_tmax = reinterpret_cast<uint32_t*>(w + wl.tmax);
-        prm.ws_share = share ? reinterpret_cast<uint64_t*>(w + wl.share) : nullptr;
+        cells = reinterpret_cast<uint64_t*>(w + wl.share);
+        prm.ws_share = share ? cells : nullptr;
+        prm.ws_arrive = fuse ? cells + kArriveWord : nullptr;
     }
     const int64_t items = batch * S;
     if (clear1 > clear0) {
         const int64_t blocks = std::min<int64_t>(ceil_div(clear1 - clear0, 256), 1024);
         hipLaunchKernelGGL(deepselect_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, hs,
-                           prm.ws_share + clear0 * kCellWords, clear1 - clear0);
+                           cells + clear0 * kCellWords, clear1 - clear0);
         if (hipGetLastError() != hipSuccess) return DS_ERR_HIP;
     }
     int rc;
@@ -2944,7 +3021,7 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
         rc = launch_all<BF16P, BF16T>(kind, units, waves, vec, prm, hs, items);
     else
         rc = launch_all<BF16T, BF16T>(kind, units, waves, vec, prm, hs, items);
-    if (prm.ws_share) {
+    if (prm.ws_share || prm.ws_arrive) {
         // a failed launch may leave a part kernel's cells without their merge
         const bool zeroed = rc == DS_OK && (eager_clear || (ws_zeroed ? *ws_zeroed : sc_zeroed && sc_zeroed->load()));
         if (ws_zeroed) *ws_zeroed = zeroed;

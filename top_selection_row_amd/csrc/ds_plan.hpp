@@ -180,6 +180,7 @@ struct WsLayout {
 // them reserved at their start, whatever the shape of the call.
 constexpr int64_t kCells = 1024;
 constexpr int64_t kCellWords = 16;  // uint64 words from one row's cell to the next
+constexpr int64_t kArriveWord = 8;  // the word of a row's cell counting its ended parts
 
 // The shared-threshold cells come first: max(batch, cells) of them, so with
 // cells = kCells the first kCells sit at the same place for every call and no
