@@ -494,13 +494,18 @@ def test_edge_lengths(dt, split, kernel, srt):
 
 
 def test_full_lengths_equal_the_plain_call():
+    # the same result set (ties included) and statistics; the unsorted order
+    # may differ, since without lengths the part that ends last merges the
+    # two parts and with them the merge kernel does
     w = synth.WORKLOADS["dsa32k"]
     x = synth.generate("dsa32k", 8)
     log("[gpu] lengths = N against no lengths")
     a = run_gpu(x, w.k, w.block, w.block2, seed=2, split=2)
     b = run_gpu_len(x, w.k, w.block, w.block2, [w.n] * 8, seed=2, split=2)
-    for u, v in zip(a, b):
-        assert np.array_equal(u, v)
+    assert np.array_equal(a[2], b[2])
+    for r in range(8):
+        oa, ob = np.argsort(a[1][r]), np.argsort(b[1][r])
+        assert np.array_equal(a[1][r][oa], b[1][r][ob]) and np.array_equal(a[0][r][oa], b[0][r][ob])
 
 
 # ---------------------------------------------------------------- fused sampling

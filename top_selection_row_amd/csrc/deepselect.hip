@@ -85,8 +85,8 @@ struct Params {
     uint32_t* ws_cnt;        // per part: its number of results
     uint32_t* ws_tkey;       // per part: its k-th key when it has k results, else 0
     uint32_t* ws_tmax;       // per part: its largest result key (0 without results)
-    uint64_t* ws_arrive;     // per row: parts ended (word kArriveWord of its cell), or NULL: merge kernel
     Layout L;
+    uint64_t* ws_arrive;     // per row: parts ended (word kArriveWord of its cell), or NULL: merge kernel
 };
 
 // Optional cycle accounting (builds with -DDS_PROFILE only): each wave adds
