@@ -495,8 +495,9 @@ def test_edge_lengths(dt, split, kernel, srt):
 
 def test_full_lengths_equal_the_plain_call():
     # the same result set (ties included) and statistics; the unsorted order
-    # may differ, since without lengths the part that ends last merges the
-    # two parts and with them the merge kernel does
+    # may differ where the two paths merge differently (rows of two bfloat16
+    # parts are merged by the part that ends last without lengths, by the
+    # merge kernel with them)
     w = synth.WORKLOADS["dsa32k"]
     x = synth.generate("dsa32k", 8)
     log("[gpu] lengths = N against no lengths")
