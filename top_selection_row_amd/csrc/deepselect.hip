@@ -2897,12 +2897,14 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
         else
             return DS_ERR_UNSUPPORTED;
     }
-    // the rows' own kernel sorts its results only when it writes the output
+    // the rows' own kernel sorts its results when it writes the output (one
+    // part per row; rows of two parts merged by their last part, below)
     const bool sort_here = sorted && S == 1;
     Layout L = make_layout(dtype, n, k, B, B2, S, waves);
     if (sort_here) L = with_sort(L, k);
     if ((int64_t)L.total > (int64_t)di.lds) return DS_ERR_UNSUPPORTED;
     bool packed = false;  // the ring kernel on packed bfloat16 entries
+    bool pair_sorts = false;  // the part kernel's layout has room to sort a merged row
     if (kind != kGeneric) {
         const bool pk = packed_parts(dtype, n, B, S);
         Layout LB = L;
@@ -2910,7 +2912,18 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
             LB = make_layout(dtype, n, k, B, B2, S, waves, true);
             if (sort_here) LB = with_sort(LB, k);
         }
-        const Layout LR = with_ring(LB, ceil_div(ceil_div(ceil_div(n, B), S), waves), units, (size_t)di.lds);
+        Layout LR = with_ring(LB, ceil_div(ceil_div(ceil_div(n, B), S), waves), units, (size_t)di.lds);
+        // sorted rows of two packed parts that the part ending last may merge:
+        // room for the sort as well, when the ring keeps its depth
+        if (sorted && S == 2 && pk && !sampling && !(opt && opt->lengths) && !share_req &&
+            (int64_t)k <= (int64_t)waves * 64 * 4 && LR.ring_depth > 0) {
+            const Layout LS =
+                with_ring(with_sort(LB, k), ceil_div(ceil_div(ceil_div(n, B), S), waves), units, (size_t)di.lds);
+            if (LS.ring_depth == LR.ring_depth) {
+                LR = LS;
+                pair_sorts = true;
+            }
+        }
         if (req_kernel == kRing && LR.ring_depth == 0) return DS_ERR_UNSUPPORTED;
         if (req_kernel == kRegs || LR.ring_depth == 0) {
             kind = kRegs;
@@ -2949,10 +2962,11 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     const bool share = share_req && S > 1 && kind == kRing &&
                        ceil_div(ceil_div(ceil_div(n, B), S), waves) >= kShareMinSteps;
     // Rows of two packed bfloat16 parts whose k results fit one merge tile,
-    // unsorted, with every part holding k results: the part that ends last
-    // merges the row (an arrival count per row in its cell), no merge kernel.
-    const bool fuse = S == 2 && kind == kRing && packed && (int64_t)k <= (int64_t)waves * 64 * 4 && !sorted &&
-                      !sampling && !(opt && opt->lengths) && !share;
+    // with every part holding k results (no lengths, no sampling): the part
+    // that ends last merges the row (an arrival count per row in its cell)
+    // and writes it, sorted when asked for; no merge kernel.
+    const bool fuse = S == 2 && kind == kRing && packed && (int64_t)k <= (int64_t)waves * 64 * 4 &&
+                      (!sorted || pair_sorts) && !sampling && !(opt && opt->lengths) && !share;
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     std::unique_lock<std::mutex> ws_lock;  // held while a library workspace is in use
