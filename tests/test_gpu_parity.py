@@ -480,10 +480,12 @@ LEN_EDGE = [0, 1, 7, 95, 96, 97, 255, 257, 600, 515, 4999, 5000, 5050, -4]
 
 @pytest.mark.parametrize("dt,split,kernel,srt", [("f32", 1, 0, False), ("bf16", 1, 0, False), ("f32", 3, 0, False),
                                                  ("bf16", 3, 0, True), ("f32", 2, 2, True), ("bf16", 2, 3, False),
-                                                 ("f32", 1, 3, True)])
+                                                 ("f32", 1, 3, True), ("bf16", 2, 1, False), ("bf16", 2, 1, True)])
 def test_edge_lengths(dt, split, kernel, srt):
     # lengths of every kind in one call: none, fewer than k, ragged inside a
-    # 16-byte load, fewer blocks than parts, N, past N and negative (clamped)
+    # 16-byte load, fewer blocks than parts, N, past N and negative (clamped);
+    # bfloat16 in two ring parts takes the merge by the part that ends last,
+    # with parts of fewer than k results, none, and no k-th key at all
     n, k, B, B2 = 5000, 96, 256, 128
     rows = len(LEN_EDGE)
     log(f"[gpu] edge lengths {dt} S={split} kernel {KERNELS.get(kernel, 'auto')} sorted={srt}")

@@ -2198,9 +2198,10 @@ __device__ __forceinline__ void load_merge_tile(MergeTile<kPkParts>& t, const Pa
     load_part_tile<NW, kPkParts>(t, p, row, (int64_t)uniform(perm[i]), (uint32_t)(tile - i * tpp));
 }
 
-// The merge of two parts of one tile each, held in registers (every part
-// holding k results): each thread keeps the results of its slots of both
-// tiles, the radix select counts them there, and only the kept ones are
+// The merge of two parts of one tile each, held in registers (ca and cb
+// results in the first and second part of the row's order): each thread
+// keeps the results of its slots of both tiles, the radix select counts them
+// there, and only the kept ones are
 // stored, in output order, to the front of the candidate buffer (write_row
 // copies them out). What it keeps, where each result lands
 // and the statistics are those of the tile loop: the buffer order it stands
@@ -2210,7 +2211,8 @@ __device__ __forceinline__ void load_merge_tile(MergeTile<kPkParts>& t, const Pa
 // histogram copies (clear on entry and on return); ends with a barrier.
 template <class D, int NW, bool kPkParts>
 __device__ __forceinline__ void merge_pair_regs(Lds<D>& s, RunState& st, const Params& p, int64_t row,
-                                                const MergeTile<kPkParts>& ta, const MergeTile<kPkParts>& tb) {
+                                                const MergeTile<kPkParts>& ta, const MergeTile<kPkParts>& tb,
+                                                uint32_t ca, uint32_t cb) {
     constexpr int E = 2 * kMT;
     const uint32_t k = (uint32_t)p.k, B2 = (uint32_t)p.B2;
     const int w = wave_id(), lane = lane_id();
@@ -2221,7 +2223,7 @@ __device__ __forceinline__ void merge_pair_regs(Lds<D>& s, RunState& st, const P
     for (int e = 0; e < E; ++e) {
         const int q = e % kMT;
         key[e] = e < kMT ? ta.key(q) : tb.key(q);
-        const bool in = (uint32_t)q * NW * 64 + threadIdx.x < k && (!st.tset || key[e] > st.tkey);
+        const bool in = (uint32_t)q * NW * 64 + threadIdx.x < (e < kMT ? ca : cb) && (!st.tset || key[e] > st.tkey);
         adm[e] = __ballot(in);
         kmax = in && key[e] > kmax ? key[e] : kmax;
         c[e / kMT] += (uint32_t)__popcll(adm[e]);
@@ -2345,15 +2347,18 @@ __device__ __forceinline__ void merge_pair_regs(Lds<D>& s, RunState& st, const P
 }
 
 // The two-part merge run by the part that ends last (packed bfloat16 parts,
-// unsorted output, every part holding k results, k at most a tile): the
-// merge kernel's register merge on an LDS view of the part kernel's layout
-// (16-bit keys in the candidate array, columns in the block ring, which both
-// hold nothing the part still needs), with the same statistics.
+// k at most a tile; parts of rows cut short by a valid length may hold fewer
+// than k results): the merge kernel's register merge on an LDS view of the
+// part kernel's layout (16-bit keys in the candidate array, columns in the
+// block ring, which both hold nothing the part still needs), with the same
+// statistics.
 template <int NW>
 __device__ void merge_in_part_kernel(unsigned char* smem, const Params& p, int64_t row) {
     Lds<BF16T> m = lds_of<BF16T>(smem, p.L);
     m.idx = reinterpret_cast<uint32_t*>(smem + p.L.ring);
     uint32_t t0 = lane_id() < 2 ? p.ws_tkey[row * 2 + lane_id()] : 0u;
+    uint32_t cnt = (uint32_t)p.k;
+    if (p.lengths && lane_id() < 2) cnt = p.ws_cnt[row * 2 + lane_id()];
     MergeTile<true> a, b;
     load_part_tile<NW, true>(a, p, row, 0, 0);
     load_part_tile<NW, true>(b, p, row, 1, 0);
@@ -2366,7 +2371,8 @@ __device__ void merge_in_part_kernel(unsigned char* smem, const Params& p, int64
     // the parts' order: (part 1, part 0) when part 1's hash is the smaller
     const uint64_t ctr0 = (uint64_t)(row * 2 + 1) << 32;
     const bool swap = splitmix_at(p.seed, ctr0 + 1u) < splitmix_at(p.seed, ctr0);
-    merge_pair_regs<BF16T, NW, true>(m, st, p, row, swap ? b : a, swap ? a : b);
+    const uint32_t c0 = uniform(__builtin_amdgcn_readlane(cnt, 0)), c1 = uniform(__builtin_amdgcn_readlane(cnt, 1));
+    merge_pair_regs<BF16T, NW, true>(m, st, p, row, swap ? b : a, swap ? a : b, swap ? c1 : c0, swap ? c0 : c1);
     uint64_t W = st.W, A = st.A, R = st.R, maxlen = st.maxlen;
     if (p.stats) {
 #pragma unroll
@@ -2555,7 +2561,7 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
         }
         DS_PROF(st, 3);
         if (regs)
-            merge_pair_regs<D, NW, kPkParts>(s, st, p, row, cur, nxt);
+            merge_pair_regs<D, NW, kPkParts>(s, st, p, row, cur, nxt, k, k);
         else
             final_select<D, NW>(s, st, k);
         DS_PROF(st, 4);
@@ -2915,7 +2921,7 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
         Layout LR = with_ring(LB, ceil_div(ceil_div(ceil_div(n, B), S), waves), units, (size_t)di.lds);
         // sorted rows of two packed parts that the part ending last may merge:
         // room for the sort as well, when the ring keeps its depth
-        if (sorted && S == 2 && pk && !sampling && !(opt && opt->lengths) && !share_req &&
+        if (sorted && S == 2 && pk && !sampling && !share_req &&
             (int64_t)k <= (int64_t)waves * 64 * 4 && LR.ring_depth > 0) {
             const Layout LS =
                 with_ring(with_sort(LB, k), ceil_div(ceil_div(ceil_div(n, B), S), waves), units, (size_t)di.lds);
@@ -2961,12 +2967,12 @@ static int topk_impl(const void* x, int dtype, int64_t batch, int64_t n, int64_t
     // two steps after it goes out): parts with fewer steps run as without it.
     const bool share = share_req && S > 1 && kind == kRing &&
                        ceil_div(ceil_div(ceil_div(n, B), S), waves) >= kShareMinSteps;
-    // Rows of two packed bfloat16 parts whose k results fit one merge tile,
-    // with every part holding k results (no lengths, no sampling): the part
-    // that ends last merges the row (an arrival count per row in its cell)
-    // and writes it, sorted when asked for; no merge kernel.
+    // Rows of two packed bfloat16 parts whose k results fit one merge tile
+    // (no sampling, no shared thresholds): the part that ends last merges the
+    // row (an arrival count per row in its cell) and writes it, sorted when
+    // asked for; no merge kernel.
     const bool fuse = S == 2 && kind == kRing && packed && (int64_t)k <= (int64_t)waves * 64 * 4 &&
-                      (!sorted || pair_sorts) && !sampling && !(opt && opt->lengths) && !share;
+                      (!sorted || pair_sorts) && !sampling && !share;
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     std::unique_lock<std::mutex> ws_lock;  // held while a library workspace is in use
