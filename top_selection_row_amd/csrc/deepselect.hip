@@ -1031,6 +1031,22 @@ struct RingStreamer {
 template <class D, int NW, int U>
 __global__ __launch_bounds__(NW * 64) void deepselect_ring_kernel(Params p);
 
+// The kernel's arguments read again from the kernel argument segment (Params
+// is a kernel's only explicit argument, at the segment's start), behind an
+// empty asm the compiler cannot look through, so that these loads are not
+// hoisted to the kernel's start: values used only at a part's end then do
+// not stay live through the step loop, where they would be spilled (the ring
+// kernels' scalar spills fall from about 180 to 80-130).
+__device__ __forceinline__ Params reload_params() {
+#if defined(__HIP_DEVICE_COMPILE__)
+    auto kp = (const __attribute__((address_space(4))) Params*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(kp));
+    return *kp;
+#else
+    return Params{};
+#endif
+}
+
 // Rows of two parts merged inside the part kernel, by the part that ends
 // last. Each part has written its results, counts and statistics; after a
 // workgroup barrier (every thread's stores done) thread 0 counts the part in
@@ -1754,13 +1770,14 @@ __global__ __launch_bounds__(NW * 64) void deepselect_ring_kernel(Params p) {
         DS_PROF(st, 14);
         final_select<D, NW>(s, st, (uint32_t)p.k, p.ws_share != nullptr);
         DS_PROF(st, 11);
-        if (p.split == 1)
-            write_row<D, NW>(s, p, g.row, st.len, st.W, st.A, st.R, st.maxlen);
+        const Params pe = reload_params();
+        if (pe.split == 1)
+            write_row<D, NW>(s, pe, g.row, st.len, st.W, st.A, st.R, st.maxlen);
         else
-            write_part<D, NW>(s, st, p, g.slot, (uint32_t)g.part_elem0);
+            write_part<D, NW>(s, st, pe, g.slot, (uint32_t)g.part_elem0);
         DS_PROF(st, 12);
         if constexpr (is_packed<D>::value) {
-            if (p.ws_arrive && arrive_last(p, g.row, s.misc + 4)) merge_in_part_kernel<NW>(smem, p, g.row);
+            if (pe.ws_arrive && arrive_last(pe, g.row, s.misc + 4)) merge_in_part_kernel<NW>(smem, pe, g.row);
         }
 #ifdef DS_PROFILE
         st.prof_flush();
@@ -2565,12 +2582,14 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
         else
             final_select<D, NW>(s, st, k);
         DS_PROF(st, 4);
+        // the arguments of the row's end, read again (see reload_params)
+        const Params pe = reload_params();
         // the parts' statistics: lane q takes parts q, q + 64, ..., then the
         // wave adds them up (only when asked for)
         uint64_t W = 0, A = 0, R = 0, maxlen = 0;
-        if (p.stats) {
+        if (pe.stats) {
             for (int32_t q = lane_id(); q < S; q += 64) {
-                const uint64_t* o = p.ws_stats + (row * S + q) * DS_STATS_PER_ROW;
+                const uint64_t* o = pe.ws_stats + (row * S + q) * DS_STATS_PER_ROW;
                 W += o[DS_STAT_W];
                 A += o[DS_STAT_A];
                 R += o[DS_STAT_R];
@@ -2590,10 +2609,10 @@ __global__ __launch_bounds__(NW * 64) void deepselect_merge_kernel(Params p) {
         R += st.R;
         maxlen = st.maxlen > maxlen ? st.maxlen : maxlen;
         DS_PROF(st, 5);
-        write_row<D, NW>(s, p, row, st.len, W, A, R, maxlen);
+        write_row<D, NW>(s, pe, row, st.len, W, A, R, maxlen);
         // every part of the row has ended (the part kernel came before): its
         // shared threshold cell is left zero for the next call
-        if (p.ws_share && threadIdx.x == 0) p.ws_share[row * kCellWords] = 0u;
+        if (pe.ws_share && threadIdx.x == 0) pe.ws_share[row * kCellWords] = 0u;
         DS_PROF(st, 6);
 #ifdef DS_PROFILE
         st.prof_flush(2048);
