@@ -990,6 +990,27 @@ def test_merge_in_part_kernel_repeats_and_graph_replays():
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("rows,n,k,waves", [(1100, 8192, 256, 8), (40, 16384, 512, 4), (40, 16384, 1536, 8)])
+def test_merge_in_part_kernel_shapes(rows, n, k, waves):
+    # rows of two bfloat16 parts merged by their last part: more rows than
+    # the 1024 reserved cells (the rest cleared by the small kernel each
+    # call), and workgroups of 4 and 8 waves; twice in a row, against the
+    # oracle and the model
+    rng = np.random.default_rng(rows + k)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((rows, n)).astype(np.float32))
+    B = 512
+    log(f"[gpu] merge in the part kernel: {rows} rows x {n}, k {k}, {waves} waves")
+    first = None
+    for rep in range(2):
+        vals, idx, st = run_gpu(x, k, B, B, seed=11, split=2, waves=waves)
+        if first is None:
+            check_rows(x, vals, idx, k)
+            check_stats_against_model(x, st, k, B, B, 11, 2, range(0, rows, max(1, rows // 4)))
+            first = (vals, idx, st)
+        else:
+            assert all(np.array_equal(a, b) for a, b in zip(first, (vals, idx, st))), "second call differs"
+
+
 def test_two_streams_at_once():
     # split calls on two streams in flight together: each stream has its own
     # library workspace, so neither call sees the other's partial results
