@@ -1034,3 +1034,28 @@ def test_two_streams_at_once():
     for ra, rb in outs:
         check_rows(xa, raw_of(ra[0]), ra[1].cpu().numpy(), w.k)
         check_rows(xb, raw_of(rb[0]), rb[1].cpu().numpy(), w.k)
+
+
+def test_two_streams_merging_in_the_part_kernel():
+    # rows of two bfloat16 parts merged by their last part, on two streams in
+    # flight together: each stream's library workspace has its own cells
+    w = synth.WORKLOADS["dsa128k_bf16"]
+    rows = 8
+    log("[gpu] two streams, rows merged in the part kernel")
+    xa = synth.generate("dsa128k_bf16", rows)
+    xb = synth.random_rows(rows, w.n, "bf16", 10, "small_ints")
+    ta, tb = to_device(xa), to_device(xb)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    sa.wait_stream(torch.cuda.current_stream())
+    sb.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for rep in range(3):
+        with torch.cuda.stream(sa):
+            ra = ds.topk(ta, w.k, w.block, w.block2, split=2)
+        with torch.cuda.stream(sb):
+            rb = ds.topk(tb, w.k, w.block, w.block2, split=2)
+        outs.append((ra, rb))
+    torch.cuda.synchronize()
+    for ra, rb in outs:
+        check_rows(xa, raw_of(ra[0]), ra[1].cpu().numpy(), w.k)
+        check_rows(xb, raw_of(rb[0]), rb[1].cpu().numpy(), w.k)
