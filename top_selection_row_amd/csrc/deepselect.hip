@@ -1118,11 +1118,15 @@ __device__ __forceinline__ void bitonic_lds(uint64_t* a, uint32_t n2) {
 // A stage of distance J < E inside each thread's E words (i0 = E * thread,
 // so word i0 + e has bit `size` set when i0 or e has).
 // The word of x and o that a side keeping the larger (big) or the smaller
-// one ends with: a 32-bit word through min and max, a 64-bit one through one
-// compare.
+// one ends with: a 32-bit word as the median of x, o and t (t all ones to
+// keep the larger, zero to keep the smaller; written as
+// max(min(x, o), min(max(x, o), t)), one v_med3_u32, with t shared by the
+// words of a stage), a 64-bit one through one compare.
 __device__ __forceinline__ uint32_t keep_side(uint32_t x, uint32_t o, bool big) {
-    const uint32_t mx = o > x ? o : x, mn = o > x ? x : o;
-    return big ? mx : mn;
+    const uint32_t t = big ? 0xFFFFFFFFu : 0u;
+    const uint32_t mn = o > x ? x : o, mx = o > x ? o : x;
+    const uint32_t c = mx < t ? mx : t;
+    return mn > c ? mn : c;
 }
 __device__ __forceinline__ uint64_t keep_side(uint64_t x, uint64_t o, bool big) {
     return (o > x) == big ? o : x;
@@ -1191,10 +1195,10 @@ __device__ __forceinline__ void bitonic_lane_stage(W (&v)[E], uint32_t i0, uint3
 
 // Register form: n2 <= E * NT words, thread t holding words E*t .. E*t+E-1
 // in v (threads past n2 / E hold padding). Within a run size, the stages go
-// j = size/2 down to 1: through LDS (buf, n2 words, between workgroup
-// barriers) while j >= 64*E, then across the lanes of the wave with vector
-// lane moves while j >= E, then inside the thread. Waves without a word only
-// take part in the barriers.
+// j = size/2 down to 1: through LDS (buf: n2 words, twice that for 32-bit
+// words; between workgroup barriers) while j >= 64*E, then across the lanes
+// of the wave with vector lane moves while j >= E, then inside the thread.
+// Waves without a word only take part in the barriers.
 template <int NW, int E, class W>
 __device__ __forceinline__ void bitonic_regs(W (&v)[E], uint32_t n2, W* buf, RunState* prof = nullptr) {
     static_assert(E == 4, "in-thread stages of distance 1 and 2");
@@ -1202,8 +1206,31 @@ __device__ __forceinline__ void bitonic_regs(W (&v)[E], uint32_t n2, W* buf, Run
     const bool holds = i0 < n2;
     const bool wave_holds = (uint32_t)wave_id() * 64u * E < n2;
     if (!wave_holds && n2 <= 64u * E) return;  // no stage through LDS: nothing to join
+    bool upper = false, entered = false;  // 32-bit words: the buffer half the next LDS stage uses; a stage ran
     for (uint32_t size = 2; size <= n2; size <<= 1) {
         uint32_t j = size >> 1;
+        if constexpr (sizeof(W) == 4) {
+            // 32-bit words: the buffer (n2 64-bit words) holds two halves of
+            // n2 words, and the stages use them in turn, so one barrier per
+            // stage is enough. A stage writes the half that the stage before
+            // the last one read, and every wave has finished those reads
+            // before it passes the last stage's barrier. The first stage
+            // waits for the buffer's earlier users.
+            for (; j >= 64u * E; j >>= 1) {
+                W* h = buf + (upper ? n2 : 0u);
+                upper = !upper;
+                if (!entered) lds_barrier();
+                entered = true;
+                if (holds) *reinterpret_cast<u32x4*>(h + i0) = u32x4{v[0], v[1], v[2], v[3]};
+                lds_barrier();
+                if (holds) {
+                    const bool big = keeps_larger(i0, j, size);  // the same for the thread's E words
+                    const u32x4 o = *reinterpret_cast<const u32x4*>(h + (i0 ^ j));
+#pragma unroll
+                    for (int e = 0; e < E; ++e) v[e] = keep_side(v[e], o[e], big);
+                }
+            }
+        }
         for (; j >= 64u * E; j >>= 1) {
             lds_barrier();  // the previous stage through LDS has been read
             if (holds) {
