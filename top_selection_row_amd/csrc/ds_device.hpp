@@ -583,6 +583,80 @@ __device__ __forceinline__ uint32_t finish_gathered(const typename D::Key* keys,
     return base;
 }
 
+// 16-bit keys spanning 256 to 4095 keys: one pass over a single histogram of
+// kWideBins 16-bit counters (the copies' 8 KiB, two bins a word, bin
+// key - base) finds the rank-th largest key, where digits of 256 bins take
+// two passes. Thread t owns the words [WPT (NT - 1 - t), + WPT), so thread 0
+// holds the top bins and an inclusive prefix of the threads' counts, taken
+// in thread order, counts the keys from the top bin down; the thread whose
+// bins hold the rank-th key names it, and the rank among the keys equal to
+// it, in folded[0, 2). Every key of keys[0, n) must lie in the window and n
+// must be under 2^16 (a counter holds a whole bin). The histogram is clear
+// on entry and cleared as it is read; tot[0, NW) carries the waves' totals.
+constexpr uint32_t kWideBins = 2 * kHistWords;
+
+template <class D, int NW>
+__device__ __forceinline__ uint32_t wide_pick(const typename D::Key* keys, uint32_t n, uint32_t base,
+                                              uint32_t* hist, uint32_t* tot, uint32_t* folded, uint32_t& rank) {
+    constexpr uint32_t NT = NW * 64, WPT = kHistWords / NT;
+    static_assert(WPT % 4 == 0 && WPT * NT == kHistWords && kHistWords == 2048, "whole 16-byte reads of the histogram");
+    const uint32_t nch = (n + kChunk - 1) / kChunk;
+    for (uint32_t c = threadIdx.x; c < nch; c += NT) {
+        KeyChunk<D> kc;
+        read_chunk<D>(kc, keys, c);
+        const uint32_t lim = n - c * kChunk;
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            const uint32_t u = chunk_key<D>(kc, i) - base;
+            // word (u >> 1) masked to the histogram (u < kWideBins already)
+            if ((uint32_t)i < lim) atomicAdd(&hist[__builtin_amdgcn_ubfe(u, 1u, 11u)], 1u << ((u & 1u) << 4));
+        }
+    }
+    lds_barrier();
+    const uint32_t w0 = WPT * (NT - 1u - threadIdx.x);
+    uint32_t cw[WPT];
+    uint32_t sum = 0;
+    u32x4* h = reinterpret_cast<u32x4*>(hist + w0);
+#pragma unroll
+    for (uint32_t j = 0; j < WPT / 4; ++j) {
+        const u32x4 v = h[j];
+        h[j] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            cw[4 * j + q] = v[q];
+            sum += (v[q] & 0xFFFFu) + (v[q] >> 16);
+        }
+    }
+    const uint32_t incl = wave_prefix_sum(sum);
+    if (lane_id() == 63) tot[wave_id()] = incl;
+    lds_barrier();
+    uint32_t above = incl - sum;  // keys in the bins above this thread's
+#pragma unroll
+    for (int v = 0; v < NW; ++v) above += v < wave_id() ? tot[v] : 0u;
+    if (above < rank && above + sum >= rank) {
+        uint32_t bin = 0, r = 0;
+        bool found = false;
+#pragma unroll
+        for (int j = (int)WPT - 1; j >= 0; --j) {
+#pragma unroll
+            for (int half = 1; half >= 0; --half) {
+                const uint32_t c = half ? cw[j] >> 16 : cw[j] & 0xFFFFu;
+                if (!found && above + c >= rank) {
+                    bin = 2u * (w0 + (uint32_t)j) + (uint32_t)half;
+                    r = rank - above;
+                    found = true;
+                }
+                above += c;
+            }
+        }
+        folded[0] = bin;
+        folded[1] = r;
+    }
+    lds_barrier();
+    rank = uniform(folded[1]);
+    return base + uniform(folded[0]);
+}
+
 // RadixSelectTopK: keep the k largest of keys/idx[0, n) (k <= n) in [0, k)
 // and return the k-th largest key. Every key lies in [lo, hi]. Entries
 // [junk, junk+64) of both arrays are scratch for dropped entries. Starts with a
@@ -603,6 +677,15 @@ __device__ uint32_t select_topk(typename D::Key* keys, uint32_t* idx, uint32_t* 
     if (!synced) lds_barrier();  // synced: the caller's own barrier made the buffer visible
     mark(5);
     uint32_t base = lo, span = hi - lo, rank = k;
+    if constexpr (D::kBits == 16) {
+        if (all_in && span >= 256u && span < kWideBins && n < 65536u) {
+            base = wide_pick<D, NW>(keys, n, lo, hist, tot, folded, rank);
+            mark(6);
+            partition_keep<D, NW>(keys, idx, tot, n, base, rank, junk);
+            mark(9);
+            return base;
+        }
+    }
     int s = span ? 32 - __clz(span) : 0;  // bit length of the span
     s = s > 8 ? s - 8 : 0;
     bool first = all_in;  // the first pass's window holds every key
