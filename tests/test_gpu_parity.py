@@ -182,6 +182,37 @@ def test_forced_waves(name, split, waves):
     check_stats_against_model(x, st, w.k, w.block, w.block2, 5, split, range(min(rows, 4)))
 
 
+def bf16_rows_of_keys(keys: np.ndarray) -> np.ndarray:
+    """bfloat16 rows (uint16 bit patterns) whose order-preserving keys are
+    `keys`, all in [0x80, 0x7FFF]: negative values, key = ~pattern, down to
+    negative infinity at key 0x7F (smaller keys would be NaN patterns)."""
+    assert keys.min() >= 0x80 and keys.max() <= 0x7FFF
+    return (0xFFFF - keys).astype(np.uint16)
+
+
+# Windows of the radix select around the widths where the pass structure
+# changes for 16-bit keys: the first compaction of a part has T unset, so
+# its window is [0, largest key] = [0, W]; at most 255 key values take one
+# 8-bit pass, 256 to 4095 one pass over a 4096-bin histogram, 4096 and more
+# two 8-bit passes. `tie` puts that share of the row on a single key, so one
+# bin's counter holds most of a buffer.
+@pytest.mark.parametrize("W,tie,waves,split", [(255, 0.0, 8, 1), (256, 0.0, 8, 1), (256, 0.0, 4, 1),
+                                               (4095, 0.0, 8, 1), (4095, 0.0, 4, 1), (4096, 0.0, 8, 1),
+                                               (3000, 0.6, 8, 1), (3000, 0.6, 4, 2), (300, 0.9, 8, 2),
+                                               (1000, 0.0, 4, 4)])
+def test_select_windows_around_the_pass_widths(W, tie, waves, split):
+    rng = np.random.default_rng(W * 131 + int(tie * 10) * 7 + waves + split)
+    rows, n, k, B, B2 = 8, 16384, 512, 1024, 1024
+    keys = rng.integers(0x80, W + 1, size=(rows, n))
+    keys[rng.random((rows, n)) < tie] = 0x80 + (W - 0x80) // 3
+    keys[:, ::97] = W  # every block holds the largest key
+    x = bf16_rows_of_keys(keys)
+    log(f"[gpu] select window W={W} tie={tie} waves={waves} S={split}")
+    vals, idx, st = run_gpu(x, k, B, B2, seed=11, split=split, waves=waves)
+    check_rows(x, vals, idx, k)
+    check_stats_against_model(x, st, k, B, B2, 11, split, range(rows))
+
+
 KERNELS = {1: "ring", 2: "registers", 3: "generic"}
 
 
