@@ -213,6 +213,25 @@ def test_select_windows_around_the_pass_widths(W, tie, waves, split):
     check_stats_against_model(x, st, k, B, B2, 11, split, range(rows))
 
 
+# Windows of more than 4095 key values once T is set (two 8-bit passes):
+# rows with keys spread over [0x80, 0x7FFF], whose second compaction's k-th
+# key lies within the top 4096 values of its window, and rows whose keys sit
+# in [0x80, 3000] but for the largest key in every block, a window set by
+# one far outlier with the k-th key near its bottom.
+@pytest.mark.parametrize("kind,waves,split", [("spread", 8, 1), ("spread", 4, 2), ("spread", 8, 4),
+                                              ("outliers", 8, 1), ("outliers", 4, 2)])
+def test_select_windows_wider_than_one_pass(kind, waves, split):
+    rng = np.random.default_rng(7 + waves + split + (100 if kind == "spread" else 0))
+    rows, n, k, B, B2 = 8, 16384, 512, 1024, 1024
+    keys = rng.integers(0x80, 0x8000 if kind == "spread" else 3001, size=(rows, n))
+    keys[:, ::97] = 0x7FFF
+    x = bf16_rows_of_keys(keys)
+    log(f"[gpu] wide select window {kind} waves={waves} S={split}")
+    vals, idx, st = run_gpu(x, k, B, B2, seed=11, split=split, waves=waves)
+    check_rows(x, vals, idx, k)
+    check_stats_against_model(x, st, k, B, B2, 11, split, range(rows))
+
+
 KERNELS = {1: "ring", 2: "registers", 3: "generic"}
 
 
