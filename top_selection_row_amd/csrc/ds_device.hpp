@@ -524,7 +524,8 @@ __device__ __forceinline__ uint32_t partition_keep(typename D::Key* keys, uint32
 // counter in *gcount, zero on entry), then after one barrier every wave
 // resolves the remaining digits of the gathered keys alone, on its own
 // 256-bin histogram (a quarter of the histogram copies, clear on entry and
-// on return): no further barrier and no fold.
+// on return): no further barrier and no fold. Once the window holds a single
+// key, that key is the answer and no further pass runs.
 template <class D, int NW>
 __device__ __forceinline__ uint32_t finish_gathered(const typename D::Key* keys, uint32_t n, uint32_t base,
                                                     uint32_t span, int s, uint32_t& rank, uint32_t* hist,
@@ -567,14 +568,23 @@ __device__ __forceinline__ uint32_t finish_gathered(const typename D::Key* keys,
     for (int j = 0; j < kGather / 64; ++j) g[j] = (uint32_t)(lane + 64 * j) < ng ? gathered[lane + 64 * j] : 0u;
     static_assert(NW * 256 <= (int)kHistWords, "a 256-bin histogram per wave must fit the histogram copies");
     uint32_t* wh = hist + wave_id() * 256;  // this wave's 256 bins
+    uint32_t cnt = ng;  // keys in the window
     while (s > 0) {
+        if (cnt == 1u) {
+            // one key left in the window: it is the k-th (rank is 1), and
+            // the remaining digits are its own
+            uint32_t mine = 0;
+#pragma unroll
+            for (int j = 0; j < kGather / 64; ++j)
+                mine = (uint32_t)(lane + 64 * j) < ng && g[j] - base <= span ? g[j] : mine;
+            return uniform(wave_max(mine));
+        }
         s = s > 8 ? s - 8 : 0;
 #pragma unroll
         for (int j = 0; j < kGather / 64; ++j) {
             const uint32_t u = g[j] - base;
             if ((uint32_t)(lane + 64 * j) < ng && u <= span) atomicAdd(&wh[(u >> s) & 255u], 1u);
         }
-        uint32_t cnt;
         const uint32_t d = pick_bin(wh, rank, cnt);
         reinterpret_cast<u32x4*>(wh)[lane] = u32x4{0u, 0u, 0u, 0u};
         base += d << s;
