@@ -525,7 +525,8 @@ __device__ __forceinline__ uint32_t partition_keep(typename D::Key* keys, uint32
 // resolves the remaining digits of the gathered keys alone, on its own
 // 256-bin histogram (a quarter of the histogram copies, clear on entry and
 // on return): no further barrier and no fold. Once the window holds a single
-// key, that key is the answer and no further pass runs.
+// key, or a pass keeps every gathered key and they are all equal, that key
+// is the answer and no further pass runs.
 template <class D, int NW>
 __device__ __forceinline__ uint32_t finish_gathered(const typename D::Key* keys, uint32_t n, uint32_t base,
                                                     uint32_t span, int s, uint32_t& rank, uint32_t* hist,
@@ -568,8 +569,20 @@ __device__ __forceinline__ uint32_t finish_gathered(const typename D::Key* keys,
     for (int j = 0; j < kGather / 64; ++j) g[j] = (uint32_t)(lane + 64 * j) < ng ? gathered[lane + 64 * j] : 0u;
     static_assert(NW * 256 <= (int)kHistWords, "a 256-bin histogram per wave must fit the histogram copies");
     uint32_t* wh = hist + wave_id() * 256;  // this wave's 256 bins
-    uint32_t cnt = ng;  // keys in the window
+    uint32_t cnt = ng;     // keys in the window
+    bool passed = false;   // a pass has narrowed the window
     while (s > 0) {
+        if (passed && cnt == ng) {
+            // the pass kept every gathered key (ties, mostly): when all of
+            // them equal the first, that key is the k-th, and rank counts
+            // the equal keys kept
+            const uint32_t g0 = uniform(__builtin_amdgcn_readfirstlane(g[0]));
+            bool other = false;
+#pragma unroll
+            for (int j = 0; j < kGather / 64; ++j) other |= (uint32_t)(lane + 64 * j) < ng && g[j] != g0;
+            if (__ballot(other) == 0ull) return g0;
+        }
+        passed = true;
         if (cnt == 1u) {
             // one key left in the window: it is the k-th (rank is 1), and
             // the remaining digits are its own
